@@ -1,0 +1,159 @@
+"""ctypes binding of libfn.so: the C entry points under the same names.
+
+Argument marshalling only: every step of the operation runs in the
+library's HIP kernels.  PyTorch supplies device memory and streams; a
+buffer argument may be a torch CUDA tensor (its data pointer is passed) or
+a raw device address as an int.  A nonzero return code raises ``FnError``
+with the library's message.  Importing this module raises ImportError if
+the library has not been built (there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # loads the HIP runtime the library binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; "
+                      f"g.build()'` from the repository root")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+FN_OK, FN_EINVAL, FN_EOVERFLOW, FN_EHIP = 0, -1, -2, -3
+FN_OUT_FP32, FN_OUT_FP16 = 0, 1
+
+# fn_sample_params: eight int32 fields, 32 bytes
+PARAMS_DTYPE = np.dtype(
+    [("flip", "<i4"), ("erase", "<i4"), ("i", "<i4"), ("j", "<i4"),
+     ("eh", "<i4"), ("ew", "<i4"), ("attempt", "<i4"), ("words_used", "<i4")]
+)
+
+_P = ctypes.c_void_p
+_u64, _i64, _i32, _f32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+_SIGS = {
+    "fn_fused_normalize": [_P, _i64, _i32, _i32, _i32, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
+                           _u64, _i32, _P, _P],
+    "fn_params": [_u64, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _f32, _f32, _P, _P],
+    "fn_test_erase_dims": [_P, _P, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _P, _P, _P, _P],
+    "fn_test_cr_ops": [_i32, _P, _P, _i64, _P, _P],
+    "fn_test_copy": [_P, _P, _i64, _P],
+}
+for _name, _args in _SIGS.items():
+    getattr(_lib, _name).argtypes = _args
+    getattr(_lib, _name).restype = ctypes.c_int
+_lib.fn_last_error.argtypes = []
+_lib.fn_last_error.restype = ctypes.c_char_p
+
+EXPORTED = ("fn_fused_normalize", "fn_params", "fn_last_error", "fn_test_erase_dims",
+            "fn_test_cr_ops", "fn_test_copy")
+
+
+class FnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libfn error {code}: {message}")
+        self.code = code
+
+
+def fn_last_error() -> str:
+    return _lib.fn_last_error().decode()
+
+
+def _addr(x) -> int | None:
+    """Device address of a torch tensor or an int (None/0 -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(rc: int) -> int:
+    if rc != FN_OK:
+        raise FnError(rc, fn_last_error())
+    return rc
+
+
+def _host_floats(v, C: int):
+    a = (ctypes.c_float * C)()
+    vals = list(v) if hasattr(v, "__len__") else [v] * C
+    if len(vals) != C:
+        raise ValueError(f"expected {C} values, got {len(vals)}")
+    for k, x in enumerate(vals):
+        a[k] = float(x)
+    return a
+
+
+def fn_fused_normalize(in_u8, N, H, W, C, mean, std, flip_p, erase_p, scale_min, scale_max,
+                       ratio_min, ratio_max, seed, out_dtype, out, stream=None) -> int:
+    return _check(_lib.fn_fused_normalize(
+        _addr(in_u8), N, H, W, C, _host_floats(mean, C), _host_floats(std, C), flip_p, erase_p,
+        scale_min, scale_max, ratio_min, ratio_max, seed & 0xFFFFFFFFFFFFFFFF, out_dtype,
+        _addr(out), _stream(stream)))
+
+
+def fn_params(seed, N, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
+              params_dev, stream=None) -> int:
+    return _check(_lib.fn_params(seed & 0xFFFFFFFFFFFFFFFF, N, H, W, flip_p, erase_p, scale_min,
+                                 scale_max, ratio_min, ratio_max, _addr(params_dev),
+                                 _stream(stream)))
+
+
+def fn_test_erase_dims(w_scale, w_ratio, count, H, W, scale_min, scale_max, ratio_min, ratio_max,
+                       eh, ew, accepted, stream=None) -> int:
+    return _check(_lib.fn_test_erase_dims(_addr(w_scale), _addr(w_ratio), count, H, W, scale_min,
+                                          scale_max, ratio_min, ratio_max, _addr(eh), _addr(ew),
+                                          _addr(accepted), _stream(stream)))
+
+
+def fn_test_cr_ops(op, a, b, count, out, stream=None) -> int:
+    return _check(_lib.fn_test_cr_ops(op, _addr(a), _addr(b), count, _addr(out), _stream(stream)))
+
+
+def fn_test_copy(src, dst, nbytes, stream=None) -> int:
+    return _check(_lib.fn_test_copy(_addr(src), _addr(dst), nbytes, _stream(stream)))
+
+
+# ------------------------------------------------------------ tensor helpers
+
+def fused_normalize(x: torch.Tensor, mean, std, flip_p=0.5, erase_p=0.0, scale=(0.02, 0.33),
+                    ratio=(0.3, 3.3), seed=0, out_dtype=FN_OUT_FP32, out=None,
+                    stream=None) -> torch.Tensor:
+    """fn_fused_normalize on an (N, H, W, C) uint8 CUDA tensor; returns (or
+    fills) the (N, H, W, C) float32/float16 output tensor."""
+    if x.dtype != torch.uint8 or x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (N, H, W, C) uint8 CUDA tensor")
+    N, H, W, C = x.shape
+    tdt = torch.float32 if out_dtype == FN_OUT_FP32 else torch.float16
+    if out is None:
+        out = torch.empty((N, H, W, C), dtype=tdt, device=x.device)
+    elif out.dtype != tdt or tuple(out.shape) != (N, H, W, C) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of the input's shape and out_dtype")
+    fn_fused_normalize(x, N, H, W, C, mean, std, flip_p, erase_p, scale[0], scale[1], ratio[0],
+                       ratio[1], seed, out_dtype, out, stream)
+    return out
+
+
+def sample_params(N, H, W, flip_p=0.5, erase_p=0.0, scale=(0.02, 0.33), ratio=(0.3, 3.3), seed=0,
+                  device="cuda", stream=None) -> torch.Tensor:
+    """fn_params into a new (N, 8) int32 CUDA tensor (fields in PARAMS_DTYPE order)."""
+    out = torch.empty((max(N, 0), 8), dtype=torch.int32, device=device)
+    fn_params(seed, N, H, W, flip_p, erase_p, scale[0], scale[1], ratio[0], ratio[1], out, stream)
+    return out
+
+
+def params_to_numpy(t: torch.Tensor) -> np.ndarray:
+    """(N, 8) int32 tensor -> structured array with PARAMS_DTYPE fields."""
+    return np.ascontiguousarray(t.cpu().numpy()).view(PARAMS_DTYPE).reshape(-1)

@@ -1,0 +1,49 @@
+"""Build libfn.so (HIP, gfx950) in place with hipcc.
+
+Flags:
+  -ffp-contract=off     the sampler's fp32 operations stay separately
+                        rounded; the pixel pass writes its fma explicitly.
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                        no packed fp32 instructions are generated.
+  -fvisibility=hidden   only the extern "C" entry points are exported.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+SOURCES = [os.path.join(HERE, "csrc", "fn_api.hip")]
+HEADERS = [os.path.join(HERE, "csrc", h) for h in ("fn_device.hpp", "fn_kernels.hpp")] + [
+    os.path.join(ROOT, "include", "fn.h")]
+LIB_PATH = os.path.join(HERE, "libfn.so")
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", f"-I{os.path.join(ROOT, 'include')}",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always recompiles) and return its path."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "packed-fp32-ops"  # the host pass does not know the target feature: harmless
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

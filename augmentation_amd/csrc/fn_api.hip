@@ -1,0 +1,256 @@
+// fn_api.hip -- the C ABI of libfn.so: argument validation, the host-side
+// constants of the operation, and kernel launches.  Declarations, argument
+// meaning, layouts and error behaviour are documented in include/fn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fn.h"
+#include "fn_kernels.hpp"
+
+#define FN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FN_OK;
+}
+
+bool in_unit(float p) { return p >= 0.0f && p <= 1.0f; }  // false for NaN
+
+// The buffer [p, p + bytes) must be device memory of the current device,
+// inside one allocation.  Failed queries leave no sticky HIP error behind.
+int check_device_range(const void* p, size_t bytes, const char* name) {
+  if (p == nullptr) return fail(FN_EINVAL, "%s is NULL", name);
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FN_EINVAL, "%s is not device memory (%s)", name, hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeDevice)
+    return fail(FN_EINVAL, "%s is not device memory (memory type %d)", name, (int)attr.type);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FN_EHIP, "hipGetDevice failed");
+  }
+  if (attr.device != dev)
+    return fail(FN_EINVAL, "%s lives on device %d, the current device is %d", name, attr.device,
+                dev);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FN_EINVAL, "%s: cannot determine its allocation (%s)", name, hipGetErrorString(e));
+  }
+  const uintptr_t lo = (uintptr_t)base, hi = lo + size, b = (uintptr_t)p;
+  if (b < lo || bytes > hi - b)
+    return fail(FN_EINVAL, "%s: %zu bytes needed, %zu available in its allocation", name, bytes,
+                (size_t)(hi - b));
+  return FN_OK;
+}
+
+int launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Sampler arguments shared by fn_params, fn_fused_normalize and the hooks.
+int make_draw_args(uint64_t seed, int32_t H, int32_t W, float flip_p, float erase_p,
+                   float scale_min, float scale_max, float ratio_min, float ratio_max,
+                   fn::DrawArgs* a) {
+  if (H <= 0 || W <= 0) return fail(FN_EINVAL, "H and W must be positive (got %d, %d)", H, W);
+  if ((int64_t)H * (int64_t)W > (int64_t)1 << 24)
+    return fail(FN_EOVERFLOW, "H*W = %lld exceeds 2^24", (long long)H * W);
+  if (!in_unit(flip_p)) return fail(FN_EINVAL, "flip_p must be in [0, 1]");
+  if (!in_unit(erase_p)) return fail(FN_EINVAL, "erase_p must be in [0, 1]");
+  if (!(scale_min >= 0x1p-30f && scale_min <= scale_max && scale_max <= 1.0f))
+    return fail(FN_EINVAL, "need 2^-30 <= scale_min <= scale_max <= 1");
+  if (!(ratio_min >= 0x1p-30f && ratio_min <= ratio_max && ratio_max <= 0x1p30f))
+    return fail(FN_EINVAL, "need 2^-30 <= ratio_min <= ratio_max <= 2^30");
+  a->seed = seed;
+  a->H = H;
+  a->W = W;
+  a->flip_p = flip_p;
+  a->erase_p = erase_p;
+  a->scale_min = scale_min;
+  a->scale_max = scale_max;
+  // RN32(ln r): the extended-precision log is far more accurate than the
+  // half-ulp margin of any fp32 rounding it could get wrong.
+  a->log_rmin = (float)logl((long double)ratio_min);
+  a->log_rmax = (float)logl((long double)ratio_max);
+  a->img_area = (float)H * (float)W;
+  return FN_OK;
+}
+
+unsigned blocks_for(int64_t items, int64_t per_block) {
+  return (unsigned)((items + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+FN_EXPORT const char* fn_last_error(void) { return g_last_error.c_str(); }
+
+FN_EXPORT int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float flip_p,
+                        float erase_p, float scale_min, float scale_max, float ratio_min,
+                        float ratio_max, fn_sample_params* params_dev, void* stream) {
+  static_assert(sizeof(fn_sample_params) == sizeof(fn::SampleParams), "layout");
+  fn::DrawArgs a;
+  int rc = make_draw_args(seed, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
+                          &a);
+  if (rc) return rc;
+  if (N < 0) return fail(FN_EINVAL, "N must be >= 0");
+  if (N > ((int64_t)1 << 36)) return fail(FN_EOVERFLOW, "N too large");
+  if (N == 0) return ok();
+  rc = check_device_range(params_dev, (size_t)N * sizeof(fn_sample_params), "params_dev");
+  if (rc) return rc;
+  const int64_t waves_per_block = fn::kBlock / 64;
+  fn::params_kernel<<<blocks_for(N, waves_per_block), fn::kBlock, 0, (hipStream_t)stream>>>(
+      a, N, reinterpret_cast<fn::SampleParams*>(params_dev));
+  return launch_status("params_kernel launch");
+}
+
+FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H, int32_t W,
+                                 int32_t C, const float* mean, const float* std, float flip_p,
+                                 float erase_p, float scale_min, float scale_max, float ratio_min,
+                                 float ratio_max, uint64_t seed, int32_t out_dtype, void* out_dev,
+                                 void* stream) {
+  fn::FusedArgs a;
+  int rc = make_draw_args(seed, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
+                          &a.draw);
+  if (rc) return rc;
+  if (C < 1 || C > 4) return fail(FN_EINVAL, "C must be in 1..4 (got %d)", C);
+  if (N < 0) return fail(FN_EINVAL, "N must be >= 0");
+  if (out_dtype != FN_OUT_FP32 && out_dtype != FN_OUT_FP16)
+    return fail(FN_EINVAL, "unknown out_dtype %d", out_dtype);
+  if (mean == nullptr || std == nullptr) return fail(FN_EINVAL, "mean and std must not be NULL");
+  for (int c = 0; c < C; ++c) {
+    if (!std::isfinite(mean[c])) return fail(FN_EINVAL, "mean[%d] is not finite", c);
+    if (!(std[c] > 0.0f) || !std::isfinite(std[c]))
+      return fail(FN_EINVAL, "std[%d] must be positive and finite", c);
+  }
+  const int64_t img = (int64_t)H * W * C;
+  if (N > INT64_MAX / 4 / img) return fail(FN_EOVERFLOW, "N*H*W*C*4 overflows int64");
+  const int64_t elems = N * img;
+  const int out_bytes = out_dtype == FN_OUT_FP32 ? 4 : 2;
+
+  // rows per work-group: about 8 KiB of input, whole rows
+  const int64_t row = (int64_t)W * C;
+  int64_t rows = (8192 + row - 1) / row;
+  if (rows > H) rows = H;
+  a.rows_per_tile = (int32_t)rows;
+  a.tiles_per_image = (int32_t)((H + rows - 1) / rows);
+  if (N > (int64_t)0x7FFFFFFF / a.tiles_per_image)
+    return fail(FN_EOVERFLOW, "N*tiles exceeds the grid size limit");
+  if (N == 0) return ok();
+
+  if ((uintptr_t)out_dev % (uintptr_t)out_bytes != 0)
+    return fail(FN_EINVAL, "out_dev must be aligned to its element size (%d bytes)", out_bytes);
+  rc = check_device_range(in_u8_dev, (size_t)elems, "in_u8_dev");
+  if (rc) return rc;
+  rc = check_device_range(out_dev, (size_t)elems * out_bytes, "out_dev");
+  if (rc) return rc;
+  const uintptr_t i0 = (uintptr_t)in_u8_dev, i1 = i0 + (uintptr_t)elems;
+  const uintptr_t o0 = (uintptr_t)out_dev, o1 = o0 + (uintptr_t)elems * out_bytes;
+  if (i0 < o1 && o0 < i1) return fail(FN_EINVAL, "input and output overlap");
+
+  a.in = in_u8_dev;
+  a.out = out_dev;
+  a.N = N;
+  a.H = H;
+  a.W = W;
+  a.C = C;
+  for (int c = 0; c < 4; ++c) {
+    if (c < C) {
+      a.mul[c] = (float)(1.0 / (255.0 * (double)std[c]));
+      a.sub[c] = (float)((double)mean[c] / (double)std[c]);
+    } else {
+      a.mul[c] = 0.0f;
+      a.sub[c] = 0.0f;
+    }
+  }
+  const unsigned grid = (unsigned)(N * a.tiles_per_image);
+  if (out_dtype == FN_OUT_FP32)
+    fn::fused_kernel<float><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(a);
+  else
+    fn::fused_kernel<_Float16><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(a);
+  return launch_status("fused_kernel launch");
+}
+
+FN_EXPORT int fn_test_erase_dims(const uint32_t* w_scale_dev, const uint32_t* w_ratio_dev,
+                                 int64_t count, int32_t H, int32_t W, float scale_min,
+                                 float scale_max, float ratio_min, float ratio_max,
+                                 int32_t* eh_dev, int32_t* ew_dev, uint8_t* accepted_dev,
+                                 void* stream) {
+  fn::DrawArgs a;
+  int rc = make_draw_args(0, H, W, 0.0f, 1.0f, scale_min, scale_max, ratio_min, ratio_max, &a);
+  if (rc) return rc;
+  if (count < 0) return fail(FN_EINVAL, "count must be >= 0");
+  if (count > ((int64_t)1 << 36)) return fail(FN_EOVERFLOW, "count too large");
+  if (count == 0) return ok();
+  if ((rc = check_device_range(w_scale_dev, count * 4, "w_scale_dev")) ||
+      (rc = check_device_range(w_ratio_dev, count * 4, "w_ratio_dev")) ||
+      (rc = check_device_range(eh_dev, count * 4, "eh_dev")) ||
+      (rc = check_device_range(ew_dev, count * 4, "ew_dev")) ||
+      (rc = check_device_range(accepted_dev, count, "accepted_dev")))
+    return rc;
+  fn::erase_dims_kernel<<<blocks_for(count, fn::kBlock), fn::kBlock, 0, (hipStream_t)stream>>>(
+      a, w_scale_dev, w_ratio_dev, count, eh_dev, ew_dev, accepted_dev);
+  return launch_status("erase_dims_kernel launch");
+}
+
+FN_EXPORT int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev, int64_t count,
+                             float* out_dev, void* stream) {
+  if (op < 0 || op > 2) return fail(FN_EINVAL, "op must be 0 (exp), 1 (sqrt) or 2 (div)");
+  if (count < 0) return fail(FN_EINVAL, "count must be >= 0");
+  if (count > ((int64_t)1 << 36)) return fail(FN_EOVERFLOW, "count too large");
+  if (count == 0) return ok();
+  int rc;
+  if ((rc = check_device_range(a_dev, count * 4, "a_dev")) ||
+      (rc = check_device_range(out_dev, count * 4, "out_dev")))
+    return rc;
+  if (op == 2 && (rc = check_device_range(b_dev, count * 4, "b_dev"))) return rc;
+  fn::cr_ops_kernel<<<blocks_for(count, fn::kBlock), fn::kBlock, 0, (hipStream_t)stream>>>(
+      op, a_dev, op == 2 ? b_dev : a_dev, count, out_dev);
+  return launch_status("cr_ops_kernel launch");
+}
+
+FN_EXPORT int fn_test_copy(const void* src_dev, void* dst_dev, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return fail(FN_EINVAL, "bytes must be a multiple of 16");
+  if (((uintptr_t)src_dev | (uintptr_t)dst_dev) & 15u)
+    return fail(FN_EINVAL, "pointers must be 16-byte aligned");
+  if (bytes == 0) return ok();
+  int rc;
+  if ((rc = check_device_range(src_dev, (size_t)bytes, "src_dev")) ||
+      (rc = check_device_range(dst_dev, (size_t)bytes, "dst_dev")))
+    return rc;
+  const uintptr_t s0 = (uintptr_t)src_dev, d0 = (uintptr_t)dst_dev;
+  if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes)
+    return fail(FN_EINVAL, "source and destination overlap");
+  const int64_t vecs = bytes / 16;
+  int64_t blocks = (vecs + fn::kBlock - 1) / fn::kBlock;
+  if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride beyond 64 work-groups per CU
+  fn::copy_kernel<<<(unsigned)blocks, fn::kBlock, 0, (hipStream_t)stream>>>(
+      reinterpret_cast<const uint4*>(src_dev), reinterpret_cast<uint4*>(dst_dev), vecs);
+  return launch_status("copy_kernel launch");
+}

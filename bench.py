@@ -1,0 +1,245 @@
+"""Benchmark: FusedNormalization throughput on one MI355X.
+
+One step = one fn_fused_normalize call over one batch of the headline
+workload: 256 images of 224x224x3 uint8 NHWC -> fp16, flip p=0.5, erase
+p=0.5, area fraction [0.02, 0.33], aspect ratio [0.3, 3.3] (the ImageNet
+training shape of page "(11) FusedNormalization", section 1; synthetic
+gradient images, no dataset).  Inputs are resident in HBM before timing;
+the timed steps rotate over --sets distinct input/output buffer sets (over
+1 GB in total) so the 256 MB Infinity Cache cannot hold the working set.
+
+Prints ONE JSON line:
+  value      images/s (whole job, one GPU)
+  roofline   algorithmic bytes per launch (every input byte read once and
+             every output element written once: N*H*W*C*(1+2)) divided by
+             the launch's average duration from HIP events around the timed
+             launches on the launch stream, against the 8 TB/s HBM peak;
+             traffic = hardware bytes per launch from the committed
+             rocprofv3 counter summary, if it was taken on the current
+             kernel source (else null)
+  cpu_baseline  the oracle (plain C loops, fp32 output) timed on this
+             host's cores over a bounded sample of the same workload.
+
+Extra legs: a plain 16-byte copy kernel moving the same byte count gives
+the practical bandwidth ceiling; --all adds one line per workload on
+stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fused_kernel_imagenet_train_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "augmentation_amd", "csrc", f)
+                  for f in ("fn_api.hip", "fn_kernels.hpp", "fn_device.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic() -> dict | None:
+    """Hardware bytes per launch from the committed counter summary, or None
+    if it is missing or was taken on other kernel sources."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    kv = {}
+    with open(PROFILE_COUNTERS) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return {"bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
+                "fetch_bytes": float(kv["fetch_bytes_per_launch"]),
+                "write_bytes": float(kv["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))  # the machine's CPU share for one GPU
+
+
+def time_launches(launch, steps: int, warmup: int, sets: int, stream) -> float:
+    """Average milliseconds per launch over `steps` launches (events on the
+    launch stream), after `warmup` untimed ones."""
+    import torch
+    for k in range(warmup):
+        launch(k % sets)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        launch(k % sets)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_workload(b, w, steps: int, warmup: int, sets: int, seed_base: int = 123) -> dict:
+    import torch
+    stream = torch.cuda.current_stream()
+    x = torch.from_numpy(w.make_input()).cuda()
+    tdt = torch.float32 if w.out_dtype == 0 else torch.float16
+    ins = [x] + [x.clone() for _ in range(sets - 1)]
+    outs = [torch.empty((w.N, w.H, w.W, w.C), dtype=tdt, device="cuda") for _ in range(sets)]
+    torch.cuda.synchronize()
+    seeds = w.seeds
+
+    def launch(k):
+        b.fn_fused_normalize(ins[k], w.N, w.H, w.W, w.C, w.mean, w.std, w.flip_p, w.erase_p,
+                             w.scale[0], w.scale[1], w.ratio[0], w.ratio[1],
+                             seeds[k % len(seeds)], w.out_dtype, outs[k], stream)
+
+    ms = time_launches(launch, steps, warmup, sets, stream)
+    del ins, outs
+    torch.cuda.empty_cache()
+    return {"ms": ms, "images_per_s": w.N / (ms * 1e-3),
+            "gbs": w.nominal_bytes / (ms * 1e-3) / 1e9}
+
+
+def bench_copy(b, nbytes: int, steps: int, warmup: int, sets: int) -> dict:
+    """The plain copy kernel moving nbytes per launch (nbytes/2 read, nbytes/2 written)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    half = (nbytes // 2) // 16 * 16
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    for s in src:
+        s.fill_(1)
+
+    def launch(k):
+        b.fn_test_copy(src[k], dst[k], half, stream)
+
+    ms = time_launches(launch, steps, warmup, sets, stream)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"ms": ms, "gbs": 2 * half / (ms * 1e-3) / 1e9, "bytes": 2 * half}
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle as it stands, on this host's cores, over whole batches of
+    the workload (fp32 output) until about budget_s seconds have passed."""
+    import oracle
+    threads = host_threads()
+    x = w.make_input()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        _, used = oracle.fused_normalize(x, w.mean, w.std, w.flip_p, w.erase_p, w.scale, w.ratio,
+                                         seed=w.seeds[0], threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    ips = reps * w.N / el
+    return {"value": round(ips, 2), "unit": "images/s", "cores": used, "kind": "oracle",
+            "sample": f"{reps} x the {w.N}-image {w.H}x{w.W}x{w.C} batch, fp32 output, "
+                      f"{used} threads, {el:.1f} s wall; CPU: {cpu_model()}",
+            "gbs_nominal": round(ips * w.H * w.W * w.C * (1 + 4) / 1e9, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=10, help="rotating buffer sets")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the operation has no cross-GPU step and this "
+              "build runs on a single MI355X (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    from augmentation_amd import binding as b
+    from augmentation_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[synth.HEADLINE]
+    r = bench_workload(b, w, args.steps, args.warmup, args.sets)
+    achieved = r["gbs"]
+    traffic = counter_traffic()
+
+    line = {
+        "metric": "images/s and % of HBM peak GB/s, 256×224²×3 u8→FP16 fused normalize",
+        "value": round(r["images_per_s"], 1),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "imagenet_train: 256x224x224x3 uint8 NHWC -> fp16 NHWC, "
+                               "flip 0.5, erase 0.5 [0.02,0.33]x[0.3,3.3], seed 123",
+                   "N": w.N, "H": w.H, "W": w.W, "C": w.C, "out": "fp16",
+                   "rotating_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),
+                     "bytes_per_launch": w.nominal_bytes},
+    }
+    if not args.no_copy:
+        c = bench_copy(b, w.nominal_bytes, args.steps, args.warmup, args.sets)
+        line["copy_ceiling"] = {"gbs": round(c["gbs"], 1), "bytes_per_launch": c["bytes"],
+                                "ms": round(c["ms"], 5),
+                                "fused_vs_copy": round(achieved / c["gbs"], 4)}
+    if args.all:
+        for name, wl in synth.WORKLOADS.items():
+            rr = bench_workload(b, wl, max(10, args.steps // 4), 5, args.sets if wl.N < 1024 else 2)
+            print(json.dumps({"workload": name, "ms_per_launch": round(rr["ms"], 5),
+                              "images_per_s": round(rr["images_per_s"], 1),
+                              "gbs_nominal": round(rr["gbs"], 1),
+                              "pct_of_peak": round(100 * rr["gbs"] / HBM_PEAK_GBS, 2)}),
+                  file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

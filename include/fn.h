@@ -1,0 +1,173 @@
+/*
+ * fn.h -- FusedNormalization on AMD Instinct MI355X (gfx950): the C ABI of libfn.so.
+ *
+ * One memory pass turns a batch of uint8 NHWC images into per-channel
+ * normalized (x/255 - mean)/std tensors in fp32 or fp16, with a per-sample
+ * random horizontal flip and a per-sample RandomErasing rectangle applied in
+ * the same pass.  The operation is the FusedNormalization step of the page
+ * "(11) FusedNormalization: fusing the last steps of data augmentation into one
+ * memory pass" (tech-renaissance.cn/blog/?p=487):
+ *   - section 5: ToTensor (x/255), RandomHorizontalFlip, Normalize
+ *     ((v - mean)/std) and RandomErasing fused into one execute() call; the
+ *     flip is drawn first, then the rectangle;
+ *   - section 6: fp32 output or fp16 output (round to nearest even);
+ *   - section 10: every random number is a pure function of (seed, offset)
+ *     through the Philox counter-based generator;
+ *   - section 12: the rectangle sampler (gate, up to 10 attempts of area
+ *     fraction and log aspect ratio, rounding, acceptance, corner).
+ * The page runs this per image on CPU threads; here one call processes a
+ * whole batch on one GPU.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device memory (hipMalloc or a PyTorch CUDA
+ *     tensor); pointers without the suffix are host memory.  All memory is
+ *     owned by the caller; the library keeps no pointer after returning and
+ *     allocates nothing.
+ *   - `stream` is a hipStream_t cast to void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously on it; the call does not synchronize.  The
+ *     caller keeps the buffers alive until the stream has finished the work.
+ *   - Return value: FN_OK (0) on success, or a negative FN_E* code.  On an
+ *     error nothing is enqueued and no output byte is written; the message is
+ *     available from fn_last_error() on the calling thread.
+ *   - All entry points are thread-safe and reentrant (no global state beyond
+ *     the thread-local error message).
+ */
+#ifndef FN_H
+#define FN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FN_OK 0
+#define FN_EINVAL (-1)    /* an argument is out of its documented domain           */
+#define FN_EOVERFLOW (-2) /* a size does not fit the index arithmetic              */
+#define FN_EHIP (-3)      /* the HIP runtime reported an error (message kept)      */
+
+/* Output element type. */
+#define FN_OUT_FP32 0 /* 4-byte IEEE binary32                                       */
+#define FN_OUT_FP16 1 /* 2-byte IEEE binary16, rounded to nearest even (page sec. 6) */
+
+/* One sample's random decisions (32 bytes, all int32):
+ *   flip        1 if the image is mirrored left-right, else 0;
+ *   erase       1 if the rectangle below is zeroed, else 0;
+ *   i, j        row and column of the rectangle's top-left corner, in output
+ *               (post-flip) coordinates; 0 when erase is 0;
+ *   eh, ew      rectangle height and width in pixels (0 < eh < H, 0 < ew < W
+ *               when erase is 1; 0 when erase is 0);
+ *   attempt     index 0..9 of the accepted attempt, or -1 when none was;
+ *   words_used  generator words the sample consumed (see fn_params). */
+typedef struct {
+    int32_t flip, erase, i, j, eh, ew, attempt, words_used;
+} fn_sample_params;
+
+/*
+ * fn_fused_normalize -- the whole operation on a batch (page sec. 5, 6, 10, 12).
+ *
+ *   in_u8_dev   N*H*W*C bytes, image n at byte offset n*H*W*C, row-major
+ *               (h, w, c) inside an image (NHWC, contiguous).  Any alignment.
+ *   N           images (N = 0: validate the arguments, enqueue nothing).
+ *   H, W, C     image height, width, channels; 1 <= C <= 4; H*W <= 2^24.
+ *   mean, std   host arrays of C floats; std[c] > 0, all finite.
+ *   flip_p      probability in [0, 1] of mirroring an image (page sec. 5
+ *               uses 0.5); 0 draws no flip word.
+ *   erase_p     probability in [0, 1] of trying to erase (page sec. 12); 0
+ *               draws no gate word.
+ *   scale_min/max  area-fraction range, 2^-30 <= scale_min <= scale_max <= 1
+ *               (page sec. 4 defaults 0.02, 0.33).
+ *   ratio_min/max  aspect-ratio range, 2^-30 <= ratio_min <= ratio_max <= 2^30
+ *               (page sec. 4 defaults 0.3, 3.3).
+ *   seed        64-bit generator key; sample n draws from the stream keyed by
+ *               (seed, n), so the result does not depend on the launch shape.
+ *   out_dtype   FN_OUT_FP32 or FN_OUT_FP16.
+ *   out_dev     N*H*W*C elements of out_dtype, same NHWC layout as the input
+ *               (C channels per pixel, no padding), aligned to the element
+ *               size (4 or 2 bytes); must not overlap the input.
+ *
+ * Result, per sample n with P = fn_params(seed, ...)[n]:
+ *   out[n,h,w,c] = +0                                 if P.erase and
+ *                                                     P.i <= h < P.i+P.eh and P.j <= w < P.j+P.ew
+ *                = x * mul_c - sub_c  (one fma)       otherwise,
+ *   x = in[n, h, P.flip ? W-1-w : w, c], mul_c = RN32(1/(255 std_c)),
+ *   sub_c = RN32(mean_c/std_c).  The pixel order is mirrored, the channel
+ *   order inside a pixel is kept (page sec. 7).  fp16 output is the fp32
+ *   value rounded to nearest even.
+ *
+ * Errors: FN_EINVAL for a null pointer (N > 0), a device pointer that is not
+ * device memory or whose buffer is shorter than the sizes above, a misaligned
+ * out_dev, any scalar outside its domain, an unknown out_dtype, or
+ * overlapping in/out;
+ * FN_EOVERFLOW for N*H*W*C*4 beyond int64 or H*W > 2^24; FN_EHIP if the
+ * launch fails.
+ */
+int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H, int32_t W, int32_t C,
+                       const float* mean, const float* std, float flip_p, float erase_p,
+                       float scale_min, float scale_max, float ratio_min, float ratio_max,
+                       uint64_t seed, int32_t out_dtype, void* out_dev, void* stream);
+
+/*
+ * fn_params -- the per-sample random decisions alone (page sec. 5 execute(),
+ * sec. 10 uniform()/randint(), sec. 12 generate_erase_rect()).
+ *
+ * Writes params_dev[n] for n in [0, N): exactly the decisions
+ * fn_fused_normalize takes with the same (seed, H, W, probabilities, ranges).
+ * Arguments as for fn_fused_normalize; params_dev holds N fn_sample_params.
+ *
+ * Generator: word k of sample n is output k%4 of Philox4x32-10 (Salmon et al.,
+ * SC'11) with counter (k/4 low, k/4 high, n low, n high) and key (seed low,
+ * seed high).  A word becomes u = (word >> 8) * 2^-24.  Words are consumed in
+ * order: the flip word (if flip_p > 0; flip iff u < flip_p), the gate word (if
+ * erase_p > 0; try iff u < erase_p), then per attempt an area-fraction word
+ * and a log-ratio word, and after an accepted attempt a row word and a column
+ * word (randint(lo, hi) = lo + floor(word * (hi-lo+1) / 2^32), inclusive).
+ * The attempt arithmetic is fp32 with one rounding per operation; exp, sqrt
+ * and division are correctly rounded; sides are rounded half away from zero.
+ *
+ * Errors: as fn_fused_normalize (params_dev must be device memory of at
+ * least N*32 bytes).
+ */
+int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float flip_p, float erase_p,
+              float scale_min, float scale_max, float ratio_min, float ratio_max,
+              fn_sample_params* params_dev, void* stream);
+
+/* The message of the last nonzero return on the calling thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char* fn_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Test and measurement hooks.  Not part of the operation; exposed so tests  */
+/* can check the building blocks exhaustively and the benchmark can measure  */
+/* a plain copy of known size.  Same conventions as above.                   */
+/* ------------------------------------------------------------------------ */
+
+/* One erase attempt (page sec. 12) per index s in [0, count): from the area
+ * word w_scale_dev[s] and the log-ratio word w_ratio_dev[s], writes the rounded
+ * sides eh_dev[s], ew_dev[s] (-1 if beyond int32) and accepted_dev[s] (1 if
+ * 0 < eh < H and 0 < ew < W).  Same domains as fn_params. */
+int fn_test_erase_dims(const uint32_t* w_scale_dev, const uint32_t* w_ratio_dev, int64_t count,
+                       int32_t H, int32_t W, float scale_min, float scale_max, float ratio_min,
+                       float ratio_max, int32_t* eh_dev, int32_t* ew_dev, uint8_t* accepted_dev,
+                       void* stream);
+
+/* The correctly rounded fp32 operations the sampler uses, per index s:
+ *   op 0: out[s] = RN32(exp(a[s]))   for |a[s]| <= 80;
+ *   op 1: out[s] = RN32(sqrt(a[s]))  for positive normal a[s];
+ *   op 2: out[s] = RN32(a[s] / b[s]) for positive normal a[s], b[s] whose
+ *         quotient is a normal float.
+ * Outside those domains the output is unspecified (but written, and the
+ * kernel still ends normally).  b_dev may be NULL for ops 0 and 1. */
+int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev, int64_t count,
+                   float* out_dev, void* stream);
+
+/* A plain 16-byte-vector device copy of `bytes` bytes (a multiple of 16, both
+ * pointers 16-byte aligned, no overlap): the reference kernel for bandwidth
+ * and for calibrating hardware byte counters. */
+int fn_test_copy(const void* src_dev, void* dst_dev, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FN_H */

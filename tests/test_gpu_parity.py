@@ -1,0 +1,318 @@
+"""GPU parity: the HIP library against the oracle, through the C ABI.
+
+Bars (checked element by element on the same seeded inputs):
+  - sample decisions (flip, erase, i, j, eh, ew, attempt, words_used):
+    bit-exact;
+  - fp32 output: |gpu - oracle| <= 2e-6, erased elements exactly +0.0;
+  - fp16 output: |gpu - oracle| <= one fp16 ulp at |oracle|, erased elements
+    exactly +0; and (informative, asserted loosely) nearly every element
+    equals the oracle rounded to nearest even.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from augmentation_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+FP32_TOL = 2e-6
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from augmentation_amd import binding
+    return binding
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def ulp16(ref: np.ndarray) -> np.ndarray:
+    """fp16 spacing at |ref| (subnormal spacing below 2^-14)."""
+    a = np.maximum(np.abs(ref.astype(np.float64)), 2.0**-14)
+    return 2.0 ** (np.floor(np.log2(a)) - 10)
+
+
+def check_values(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
+    """Compare a GPU output (fp32 or fp16) with the oracle's fp32 result."""
+    assert got.shape == ref.shape, what
+    zero = ref.view(np.uint32) == 0
+    if got.dtype == np.float32:
+        err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        assert float(err.max(initial=0.0)) <= FP32_TOL, (what, float(err.max()))
+        assert np.all(got.view(np.uint32)[zero] == 0), what
+        return {"max_abs": float(err.max(initial=0.0))}
+    assert got.dtype == np.float16
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    bad = err > ulp16(ref)
+    assert not np.any(bad), (what, int(bad.sum()), float(err.max()))
+    assert np.all(got.view(np.uint16)[zero] == 0), what
+    same = float(np.mean(got.view(np.uint16) == ref.astype(np.float16).view(np.uint16)))
+    assert same >= 0.9999, (what, same)  # a round-toward-zero conversion would give ~0.5
+    return {"max_abs": float(err.max(initial=0.0)), "rne_equal": same}
+
+
+def run_fused(b, xt, N, H, W, C, w_or_kw, seed, out_dtype, out=None, stream=None):
+    w = w_or_kw
+    tdt = torch.float32 if out_dtype == 0 else torch.float16
+    if out is None:
+        out = torch.empty((N, H, W, C), dtype=tdt, device="cuda")
+    b.fn_fused_normalize(xt, N, H, W, C, w["mean"], w["std"], w["flip_p"], w["erase_p"],
+                         w["scale"][0], w["scale"][1], w["ratio"][0], w["ratio"][1], seed,
+                         out_dtype, out, stream)
+    return out
+
+
+def wl_dict(w: synth.Workload) -> dict:
+    return dict(mean=w.mean, std=w.std, flip_p=w.flip_p, erase_p=w.erase_p, scale=w.scale,
+                ratio=w.ratio)
+
+
+def gpu_params(b, w: synth.Workload, seed: int) -> np.ndarray:
+    t = b.sample_params(w.N, w.H, w.W, w.flip_p, w.erase_p, w.scale, w.ratio, seed)
+    torch.cuda.synchronize()
+    return b.params_to_numpy(t)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_params_bit_exact(b, name):
+    w = synth.WORKLOADS[name]
+    for seed in w.seeds:
+        say(f"params: {name} N={w.N} {w.H}x{w.W} seed={seed}")
+        got = gpu_params(b, w, seed)
+        ref = oracle.params(seed, 0, w.N, w.H, w.W, w.flip_p, w.erase_p, w.scale, w.ratio)
+        rows = np.flatnonzero(np.any(got.view(np.int32).reshape(-1, 8) !=
+                                     ref.view(np.int32).reshape(-1, 8), axis=1))
+        assert rows.size == 0, (name, seed, rows.size, rows[:5], got[rows[:3]], ref[rows[:3]])
+
+
+@pytest.mark.parametrize("name", ["mnist", "cifar", "imagenet_train", "imagenet_val"])
+def test_fused_full_batch(b, name):
+    w = synth.WORKLOADS[name]
+    x = w.make_input()
+    seed = w.seeds[0]
+    say(f"fused: {name} {x.shape} out_dtype={w.out_dtype} seed={seed}")
+    xt = torch.from_numpy(x).cuda()
+    out = run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), seed, w.out_dtype)
+    torch.cuda.synchronize()
+    ref, _ = oracle.fused_normalize(x, w.mean, w.std, w.flip_p, w.erase_p, w.scale, w.ratio,
+                                    seed=seed, threads=THREADS)
+    stats = check_values(out.cpu().numpy(), ref, name)
+    say(f"  {stats}")
+    # the other dtype on the same inputs
+    other = 1 - w.out_dtype
+    out2 = run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), seed, other)
+    torch.cuda.synchronize()
+    check_values(out2.cpu().numpy(), ref, name + " other dtype")
+
+
+def test_stress_eight_back_to_back_launches(b):
+    """2048 images, eight launches on one stream with seeds 123..130 into
+    eight distinct outputs; every launch's decisions are checked in full,
+    and a sample of images per launch element by element."""
+    w = synth.WORKLOADS["stress"]
+    x = w.make_input()
+    xt = torch.from_numpy(x).cuda()
+    say(f"stress: {x.shape} x{w.launches} launches")
+    outs = [torch.empty((w.N, w.H, w.W, w.C), dtype=torch.float16, device="cuda")
+            for _ in w.seeds]
+    for seed, out in zip(w.seeds, outs):
+        run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), seed, w.out_dtype, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    for seed, out in zip(w.seeds, outs):
+        P = oracle.params(seed, 0, w.N, w.H, w.W, w.flip_p, w.erase_p, w.scale, w.ratio)
+        got_p = gpu_params(b, w, seed)
+        assert got_p.tobytes() == P.tobytes(), seed
+        picks = sorted({0, 1, w.N - 1, *rng.choice(w.N, 9, replace=False).tolist()})
+        idx = torch.tensor(picks, device="cuda")
+        got = out.index_select(0, idx).cpu().numpy()
+        for k, n in enumerate(picks):
+            ref, _ = oracle.fused_normalize(x[n:n + 1], w.mean, w.std, w.flip_p, w.erase_p,
+                                            w.scale, w.ratio, seed=seed, first_n=n)
+            check_values(got[k:k + 1], ref, f"stress seed={seed} n={n}")
+        say(f"  seed {seed}: {int(P['flip'].sum())} flipped, {int(P['erase'].sum())} erased, "
+            f"sampled {picks}")
+
+
+EDGE_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1, 3),
+               (1, 1, 17, 3), (5, 17, 1, 3), (3, 2, 2, 1), (2, 31, 33, 3), (7, 13, 11, 4),
+               (2, 4, 8192, 1), (1, 600, 6, 3), (9, 28, 28, 1), (64, 32, 32, 3)]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES)
+@pytest.mark.parametrize("out_dtype", [0, 1])
+def test_edge_shapes_misaligned_with_guards(b, shape, out_dtype):
+    N, H, W, C = shape
+    rng = np.random.default_rng(sum(shape) + out_dtype)
+    x = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    mean = tuple(float(v) for v in rng.uniform(0.3, 0.6, C))
+    std = tuple(float(v) for v in rng.uniform(0.2, 0.3, C))
+    kw = dict(mean=mean, std=std, flip_p=0.5, erase_p=1.0, scale=(0.02, 0.33), ratio=(0.3, 3.3))
+    elems = N * H * W * C
+    esz = 4 if out_dtype == 0 else 2
+    in_off = 1 + (sum(shape) % 7)          # input at a byte offset in 1..7
+    out_off = 4096 + esz                   # output element-aligned, not 16-aligned
+    guard = 4096
+    say(f"edge: shape={shape} out_dtype={out_dtype} in_off={in_off}")
+    in_buf = torch.zeros(elems + in_off + 64, dtype=torch.uint8, device="cuda")
+    in_buf[in_off:in_off + elems] = torch.from_numpy(x.reshape(-1)).cuda()
+    out_buf = torch.full((out_off + elems * esz + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    seed = 1000 + N
+    b.fn_fused_normalize(in_buf.data_ptr() + in_off, N, H, W, C, mean, std, kw["flip_p"],
+                         kw["erase_p"], 0.02, 0.33, 0.3, 3.3, seed, out_dtype,
+                         out_buf.data_ptr() + out_off)
+    torch.cuda.synchronize()
+    host = out_buf.cpu().numpy()
+    assert np.all(host[:out_off] == 0xA5) and np.all(host[out_off + elems * esz:] == 0xA5)
+    got = host[out_off:out_off + elems * esz].view(np.float32 if out_dtype == 0 else np.float16)
+    ref, _ = oracle.fused_normalize(x, mean, std, kw["flip_p"], kw["erase_p"], seed=seed)
+    check_values(got.reshape(shape), ref, str(shape))
+
+
+def test_largest_image(b):
+    """H*W = 2^24, the largest image the sampler's exact area allows."""
+    N, H, W, C = 1, 4096, 4096, 3
+    x = np.random.default_rng(5).integers(0, 256, size=(N, H, W, C), dtype=np.uint8)
+    say(f"largest: {x.shape}")
+    xt = torch.from_numpy(x).cuda()
+    kw = dict(mean=synth.IMAGENET_MEAN, std=synth.IMAGENET_STD, flip_p=1.0, erase_p=1.0,
+              scale=synth.ERASE_SCALE, ratio=synth.ERASE_RATIO)
+    out = run_fused(b, xt, N, H, W, C, kw, 77, 1)
+    torch.cuda.synchronize()
+    ref, _ = oracle.fused_normalize(x, kw["mean"], kw["std"], 1.0, 1.0, seed=77, threads=THREADS)
+    check_values(out.cpu().numpy(), ref, "4096x4096x3")
+
+
+def test_zero_images_writes_nothing(b):
+    out = torch.full((64,), 7.0, device="cuda")
+    b.fn_fused_normalize(0, 0, 8, 8, 3, (0.5,) * 3, (0.25,) * 3, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, 1,
+                         0, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_result_independent_of_batch_size_and_repeatable(b):
+    w = synth.WORKLOADS["cifar"]
+    x = w.make_input()
+    xt = torch.from_numpy(x).cuda()
+    full = run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), 5, 0)
+    again = run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), 5, 0)
+    head = run_fused(b, xt[:10].contiguous(), 10, w.H, w.W, w.C, wl_dict(w), 5, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int32), again.view(torch.int32))
+    assert torch.equal(full[:10].view(torch.int32), head.view(torch.int32))
+
+
+def test_page_fp32_vs_fp16_consistency(b):
+    """Page "(11)" section 13: 28x28 grey batch, fp32 and fp16 outputs agree
+    to MSE < 1e-5 and max relative error < 1e-3 over |v| > 1e-6."""
+    w = synth.WORKLOADS["mnist"]
+    xt = torch.from_numpy(w.make_input()).cuda()
+    o32 = run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), 123, 0).cpu().numpy().astype(np.float64)
+    o16 = run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), 123, 1).cpu().numpy().astype(np.float64)
+    keep = np.abs(o32) > 1e-6
+    assert np.mean((o32 - o16) ** 2) < 1e-5
+    assert np.max(np.abs(o32[keep] - o16[keep]) / np.abs(o32[keep])) < 1e-3
+
+
+@pytest.mark.parametrize("ratio", [(0.3, 3.3), (0.5, 4.0), (1.0, 1.0), (2.0**-30, 2.0**30)])
+def test_erase_attempts_exhaustive_over_ratio_words(b, ratio):
+    """Every one of the 2^24 log-ratio draws (random area words): sides and
+    acceptance bit-exact against the oracle."""
+    n = 2**24
+    rng = np.random.default_rng(len(str(ratio)))
+    w_ratio = (np.arange(n, dtype=np.uint64) << np.uint64(8) | rng.integers(0, 256, n, dtype=np.uint64)).astype(np.uint32)
+    w_scale = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
+    H, W = 224, 224
+    say(f"erase dims: ratio={ratio}")
+    ws, wr = torch.from_numpy(w_scale).cuda(), torch.from_numpy(w_ratio).cuda()
+    eh = torch.empty(n, dtype=torch.int32, device="cuda")
+    ew = torch.empty(n, dtype=torch.int32, device="cuda")
+    acc = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b.fn_test_erase_dims(ws, wr, n, H, W, 0.02, 0.33, ratio[0], ratio[1], eh, ew, acc)
+    torch.cuda.synchronize()
+    r_eh, r_ew, r_acc = oracle.erase_dims_array(w_scale, w_ratio, H, W, (0.02, 0.33), ratio)
+    np.testing.assert_array_equal(eh.cpu().numpy(), r_eh)
+    np.testing.assert_array_equal(ew.cpu().numpy(), r_ew)
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(bool), r_acc)
+
+
+def test_correctly_rounded_ops(b):
+    rng = np.random.default_rng(8)
+    # exp: a strided sweep over every binade of 2^-30 <= |L| <= 46, both signs
+    bits = np.arange(0x30800000, 0x42380000, 31, dtype=np.uint32)
+    L = np.concatenate([bits, bits | np.uint32(0x80000000)]).view(np.float32)
+    # sqrt: strided sweep over all positive normal floats
+    sq = np.arange(0x00800000, 0x7F800000, 101, dtype=np.uint32).view(np.float32)
+    # division: random positive normal pairs with a normal quotient
+    a = rng.integers(0x00800000, 0x7F800000, 10_000_000, dtype=np.uint32).view(np.float32)
+    d = rng.integers(0x00800000, 0x7F800000, 10_000_000, dtype=np.uint32).view(np.float32)
+    with np.errstate(over="ignore", under="ignore"):
+        q = a / d
+    keep = (q >= np.float32(2.0**-126)) & np.isfinite(q)
+    a, d, q = a[keep], d[keep], q[keep]
+    for op, x, y, ref in ((0, L, None, oracle.expf_array(L)), (1, sq, None, np.sqrt(sq)),
+                          (2, a, d, q)):
+        say(f"cr op {op}: {x.size} values")
+        xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        yt = torch.from_numpy(np.ascontiguousarray(y)).cuda() if y is not None else None
+        out = torch.empty_like(xt)
+        b.fn_test_cr_ops(op, xt, yt, x.size, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        bad = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+        assert bad.size == 0, (op, x[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def test_bad_pointers_rejected_without_launch(b):
+    x = torch.zeros(2 * 8 * 8 * 3, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(2 * 8 * 8 * 3, dtype=torch.float32, device="cuda")
+    host = np.zeros(2 * 8 * 8 * 3 * 4, np.uint8)
+    args = ((0.5,) * 3, (0.25,) * 3, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, 1, 0)
+    # an allocation of exactly 1000 bytes, straight from the HIP runtime torch uses
+    import ctypes
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    raw = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(raw), ctypes.c_size_t(1000)) == 0
+    try:
+        cases = {
+            "host input": (host.ctypes.data, out),
+            "host output": (x, host.ctypes.data),
+            "output past the end of its allocation": (x, raw.value + 1000 - 64),
+            "misaligned fp32 output": (x, out.data_ptr() + 2),
+            "overlap": (out.view(torch.uint8), out),
+        }
+        for what, (src, dst) in cases.items():
+            say(f"bad pointer: {what}")
+            with pytest.raises(b.FnError) as e:
+                b.fn_fused_normalize(src, 2, 8, 8, 3, *args, dst)
+            assert e.value.code == b.FN_EINVAL, what
+        # the same raw allocation, used within its size, is accepted
+        b.fn_fused_normalize(x, 1, 8, 5, 3, *args, raw.value)
+        torch.cuda.synchronize()
+    finally:
+        hip.hipFree(raw)
+    # no sticky HIP error is left behind: torch keeps working
+    y = (x.float() + 1).sum()
+    torch.cuda.synchronize()
+    assert float(y) == x.numel()
+
+
+def test_copy_hook(b):
+    n = (1 << 20) + 16 * 37
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    b.fn_test_copy(src, dst, n)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
