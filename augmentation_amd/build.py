@@ -3,6 +3,9 @@
 Flags:
   -ffp-contract=off     the sampler's fp32 operations stay separately
                         rounded; the pixel pass writes its fma explicitly.
+  -fhip-fp32-correctly-rounded-divide-sqrt
+                        fp32 '/' and sqrtf are IEEE correctly rounded (the
+                        sampler's decisions depend on it).
   -Xclang -target-feature -Xclang -packed-fp32-ops
                         no packed fp32 instructions are generated.
   -fvisibility=hidden   only the extern "C" entry points are exported.
@@ -17,13 +20,14 @@ ROOT = os.path.dirname(HERE)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = [os.path.join(HERE, "csrc", "fn_api.hip")]
-HEADERS = [os.path.join(HERE, "csrc", h) for h in ("fn_device.hpp", "fn_kernels.hpp")] + [
+HEADERS = [os.path.join(HERE, "csrc", h) for h in ("fn_device.hpp", "fn_kernels.hpp",
+                                                   "exp2_table.inc")] + [
     os.path.join(ROOT, "include", "fn.h")]
 LIB_PATH = os.path.join(HERE, "libfn.so")
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
-    "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", f"-I{os.path.join(ROOT, 'include')}",
 ]
 

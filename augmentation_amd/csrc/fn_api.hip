@@ -3,6 +3,7 @@
 // meaning, layouts and error behaviour are documented in include/fn.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -13,6 +14,10 @@
 #include "fn_kernels.hpp"
 
 #define FN_EXPORT extern "C" __attribute__((visibility("default")))
+
+#ifndef FN_USE_GROUPED
+#define FN_USE_GROUPED 0
+#endif
 
 namespace {
 
@@ -107,6 +112,142 @@ unsigned blocks_for(int64_t items, int64_t per_block) {
   return (unsigned)((items + per_block - 1) / per_block);
 }
 
+// Compute units of the current device, queried once per device.
+int device_cu_count(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FN_EHIP, "hipGetDevice failed");
+  }
+  if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed) > 0) {
+    *cus = cache[dev].load(std::memory_order_relaxed);
+    return FN_OK;
+  }
+  int v = 0;
+  const hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || v <= 0) {
+    (void)hipGetLastError();
+    return fail(FN_EHIP, "cannot query the compute unit count: %s", hipGetErrorString(e));
+  }
+  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  *cus = v;
+  return FN_OK;
+}
+
+// Most images a run of `tiles` consecutive tiles can touch.
+int64_t max_images_per_range(const fn::FusedArgs& a, int64_t tiles) {
+  if (a.images_per_tile > 1) return tiles * a.images_per_tile;
+  return (tiles + a.tiles_per_image - 1) / a.tiles_per_image + 1;
+}
+
+// Tile plan of the rows kernel: whole rows, about kTileBytesTarget input
+// bytes per tile, smaller when the batch is too small to give every compute
+// unit kWgPerCu tiles.  Sets the tile fields of `a`.
+int plan_rows_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elems, int cus) {
+  int64_t target = fn::kTileBytesTarget;
+  const int64_t want = (int64_t)cus * fn::kMinTilesPerCu;
+  if (elems / want < target) target = elems / want;
+  if (target < row) target = row;
+  const int64_t image_bytes = (int64_t)H * row;
+  int64_t tile_bytes;
+  if (image_bytes <= target) {
+    int64_t g = target / image_bytes;
+    if (g > fn::kMaxImagesPerBlock) g = fn::kMaxImagesPerBlock;
+    a->images_per_tile = (int32_t)g;
+    a->rows_per_tile = H;
+    a->tiles_per_image = 1;
+    a->total_tiles = (N + g - 1) / g;
+    tile_bytes = g * image_bytes;
+  } else {
+    int64_t r = target / row;
+    if (r < 1) r = 1;
+    if (r > H) r = H;
+    a->images_per_tile = 1;
+    a->rows_per_tile = (int32_t)r;
+    a->tiles_per_image = (int32_t)((H + r - 1) / r);
+    a->total_tiles = N * a->tiles_per_image;
+    tile_bytes = r * row;
+  }
+  if (tile_bytes > fn::kTileBytesMax) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
+  a->lds_buffer_bytes = (int32_t)((tile_bytes + 32 + 15) / 16 * 16);
+  return FN_OK;
+}
+
+fn::FastDiv make_fast_div(uint32_t d) {
+  fn::FastDiv f;
+  f.d = d;
+  f.m = d > 1 ? (uint32_t)((((uint64_t)1) << 32) / d + 1) : 0u;
+  return f;
+}
+
+// Pixels per lane group for the grouped kernel, or 0 if it does not apply:
+// W must be a multiple of the group, the input aligned to the group's load
+// vector (16, 8 or 4 bytes), and the output 16-byte aligned with a group
+// size that is a multiple of 4 bytes.  Prefers the widest group.
+int pick_group_pixels(int32_t W, int32_t C, int out_bytes, uintptr_t in, uintptr_t out) {
+  if (out % 16 != 0) return 0;
+  const int choices[3] = {16, 8, 4};
+  for (int px : choices) {
+    if (px > fn::kGroupPxMax) continue;
+    if (W % px != 0) continue;
+    const int nb = px * C;
+    const int align = nb % 16 == 0 ? 16 : (nb % 8 == 0 ? 8 : 4);
+    if (nb % 4 != 0 || in % (uintptr_t)align != 0) continue;
+    if ((nb * out_bytes) % 4 != 0) continue;
+    return px;
+  }
+  return 0;
+}
+
+template <int C, int PX>
+void launch_grouped_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, hipStream_t st) {
+  if (out_dtype == FN_OUT_FP32)
+    fn::fused_grouped_kernel<C, PX, float><<<grid, fn::kBlock, 0, st>>>(a);
+  else
+    fn::fused_grouped_kernel<C, PX, _Float16><<<grid, fn::kBlock, 0, st>>>(a);
+}
+
+template <int PX>
+void launch_grouped_px(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid,
+                       hipStream_t st) {
+  switch (C) {
+    case 1: launch_grouped_c<1, PX>(a, out_dtype, grid, st); break;
+    case 2: launch_grouped_c<2, PX>(a, out_dtype, grid, st); break;
+    case 3: launch_grouped_c<3, PX>(a, out_dtype, grid, st); break;
+    default: launch_grouped_c<4, PX>(a, out_dtype, grid, st); break;
+  }
+}
+
+template <int C>
+void launch_rows_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t lds,
+                   hipStream_t st) {
+  if (out_dtype == FN_OUT_FP32)
+    fn::fused_rows_kernel<C, float><<<grid, fn::kRowsBlock, lds, st>>>(a);
+  else
+    fn::fused_rows_kernel<C, _Float16><<<grid, fn::kRowsBlock, lds, st>>>(a);
+}
+
+void launch_rows(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
+                 hipStream_t st) {
+  switch (C) {
+    case 1: launch_rows_c<1>(a, out_dtype, grid, lds, st); break;
+    case 2: launch_rows_c<2>(a, out_dtype, grid, lds, st); break;
+    case 3: launch_rows_c<3>(a, out_dtype, grid, lds, st); break;
+    default: launch_rows_c<4>(a, out_dtype, grid, lds, st); break;
+  }
+}
+
+void launch_grouped(const fn::FusedArgs& a, int C, int px, int out_dtype, unsigned grid,
+                    hipStream_t st) {
+  if (px == 16)
+    launch_grouped_px<16>(a, C, out_dtype, grid, st);
+  else if (px == 8)
+    launch_grouped_px<8>(a, C, out_dtype, grid, st);
+  else
+    launch_grouped_px<4>(a, C, out_dtype, grid, st);
+}
+
 }  // namespace
 
 FN_EXPORT const char* fn_last_error(void) { return g_last_error.c_str(); }
@@ -124,8 +265,8 @@ FN_EXPORT int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float fl
   if (N == 0) return ok();
   rc = check_device_range(params_dev, (size_t)N * sizeof(fn_sample_params), "params_dev");
   if (rc) return rc;
-  const int64_t waves_per_block = fn::kBlock / 64;
-  fn::params_kernel<<<blocks_for(N, waves_per_block), fn::kBlock, 0, (hipStream_t)stream>>>(
+  const int64_t samples_per_block = fn::kBlock / 16;
+  fn::params_kernel<<<blocks_for(N, samples_per_block), fn::kBlock, 0, (hipStream_t)stream>>>(
       a, N, reinterpret_cast<fn::SampleParams*>(params_dev));
   return launch_status("params_kernel launch");
 }
@@ -154,7 +295,7 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
   const int64_t elems = N * img;
   const int out_bytes = out_dtype == FN_OUT_FP32 ? 4 : 2;
 
-  // rows per work-group: about 8 KiB of input, whole rows
+  // generic kernel tiles: about 8 KiB of input, whole rows
   const int64_t row = (int64_t)W * C;
   int64_t rows = (8192 + row - 1) / row;
   if (rows > H) rows = H;
@@ -183,18 +324,64 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
   for (int c = 0; c < 4; ++c) {
     if (c < C) {
       a.mul[c] = (float)(1.0 / (255.0 * (double)std[c]));
-      a.sub[c] = (float)((double)mean[c] / (double)std[c]);
+      a.nsub[c] = -(float)((double)mean[c] / (double)std[c]);
     } else {
       a.mul[c] = 0.0f;
-      a.sub[c] = 0.0f;
+      a.nsub[c] = 0.0f;
+    }
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  a.total_bytes = elems;
+  if (!FN_USE_GROUPED && (uintptr_t)out_dev % 16 == 0 && row % (16 / out_bytes) == 0 &&
+      row <= fn::kTileBytesMax) {
+    int cus = 0;
+    rc = device_cu_count(&cus);
+    if (rc) return rc;
+    rc = plan_rows_tiles(&a, N, H, row, elems, cus);
+    if (rc) return rc;
+    int64_t cap = fn::kWgPerCu > 0 ? (int64_t)cus * fn::kWgPerCu : a.total_tiles;
+    if (cap > 0x7FFFFFFF) cap = 0x7FFFFFFF;
+    unsigned g = (unsigned)(a.total_tiles < cap ? a.total_tiles : cap);
+    // no work-group may touch more images than it has decision slots
+    while ((int64_t)g < a.total_tiles && max_images_per_range(a, (a.total_tiles + g - 1) / g) >
+                                    fn::kMaxImagesPerBlock)
+      g = (unsigned)((int64_t)g * 2 > a.total_tiles ? a.total_tiles : (int64_t)g * 2);
+    if (max_images_per_range(a, (a.total_tiles + g - 1) / g) > fn::kMaxImagesPerBlock)
+      return fail(FN_EOVERFLOW, "tile plan exceeds the per-work-group image limit");
+    a.div_row = make_fast_div((uint32_t)row);
+    a.div_h = make_fast_div((uint32_t)H);
+    launch_rows(a, C, out_dtype, g, 2 * (size_t)a.lds_buffer_bytes, st);
+    return launch_status("fused_rows_kernel launch");
+  }
+  const int px = pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);
+  if (px > 0) {
+    a.groups_per_row = (uint32_t)(W / px);
+    a.groups_per_image = (uint32_t)((int64_t)H * W / px);
+    a.total_groups = N * (int64_t)a.groups_per_image;
+    a.div_gpi = make_fast_div(a.groups_per_image);
+    a.div_gpr = make_fast_div(a.groups_per_row);
+    // groups per lane: as many as allowed while one work-group touches at
+    // most kMaxImagesPerBlock images
+    int iter = fn::kMaxIter;
+    while (iter > 1 && (int64_t)fn::kBlock * iter > (int64_t)(fn::kMaxImagesPerBlock - 1) *
+                                                         a.groups_per_image)
+      --iter;
+    if ((int64_t)fn::kBlock * iter <= (int64_t)(fn::kMaxImagesPerBlock - 1) * a.groups_per_image) {
+      a.iter = iter;
+      const int64_t per_block = (int64_t)fn::kBlock * iter;
+      const int64_t grid = (a.total_groups + per_block - 1) / per_block;
+      if (grid > 0x7FFFFFFF) return fail(FN_EOVERFLOW, "grid size limit exceeded");
+      launch_grouped(a, C, px, out_dtype, (unsigned)grid, st);
+      return launch_status("fused_grouped_kernel launch");
     }
   }
   const unsigned grid = (unsigned)(N * a.tiles_per_image);
   if (out_dtype == FN_OUT_FP32)
-    fn::fused_kernel<float><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(a);
+    fn::fused_generic_kernel<float><<<grid, fn::kBlock, 0, st>>>(a);
   else
-    fn::fused_kernel<_Float16><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(a);
-  return launch_status("fused_kernel launch");
+    fn::fused_generic_kernel<_Float16><<<grid, fn::kBlock, 0, st>>>(a);
+  return launch_status("fused_generic_kernel launch");
 }
 
 FN_EXPORT int fn_test_erase_dims(const uint32_t* w_scale_dev, const uint32_t* w_ratio_dev,

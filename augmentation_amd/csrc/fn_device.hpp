@@ -70,23 +70,38 @@ __device__ __forceinline__ int32_t word_randint(int32_t lo, int32_t hi, uint32_t
 
 // ---------------------------------------------------------------------------
 // Correctly rounded fp32 exp for |L| <= 80, integer fixed point.
-//   L is converted exactly to Q96; k = floor(L / ln 2) and r = L - k ln 2 in
-//   [0, ln 2) use ln 2 to 96 fraction bits; e^r comes from its Taylor series
-//   to the 1/19! term by Horner's rule in Q62 with r in Q64; the result is
-//   rounded to 24 bits (nearest even) and scaled by 2^k.
-//   Error of e^r before rounding: below 5 units of 2^-62 from the Horner
-//   truncations and coefficient roundings (each step's error is damped by
-//   r < 0.7), 2^-71 from the series tail, 2^-64 from truncating r: relative
-//   error < 2^-59.5.  The rounding is therefore correct whenever e^L is not
-//   within 2^-59.5 (relative) of a midpoint between two floats.
+//   L is converted exactly to Q96.  With step = ln 2 / 32 (to 96 fraction
+//   bits), k = floor(L / step) and r = L - k step in [0, step); then
+//   e^L = 2^(k >> 5) * 2^((k & 31)/32) * e^r.  e^r comes from its Taylor
+//   series to the 1/8! term by Horner's rule in Q62 with r in Q64; the table
+//   entry 2^(j/32) is the exactly rounded Q62 value; the product is rounded
+//   to 24 bits (nearest even).
+//   Error before the final rounding: the Horner truncations and coefficient
+//   roundings stay below 1.6 units of 2^-62 (each step's error is damped by
+//   r < 0.022), the series tail below 2^-68, truncating r to Q64 2^-64, the
+//   table entry half a unit and the product's truncation one unit: relative
+//   error < 2^-59.8.  The rounding is therefore correct whenever e^L is not
+//   within 2^-59.8 (relative) of a midpoint between two floats.
 // ---------------------------------------------------------------------------
-constexpr uint64_t factorial(int j) { return j <= 1 ? 1ull : (uint64_t)j * factorial(j - 1); }
-// round(2^62 / j!)
-constexpr uint64_t inv_factorial_q62(int j) {
-  return ((1ull << 62) + factorial(j) / 2) / factorial(j);
-}
+#include "exp2_table.inc"
 
-__device__ __forceinline__ float cr_expf(float L) {
+// Taylor coefficients, built at compile time: round(2^62 / j!) for the exact
+// path and 1/j! rounded to double for the fast path.
+struct InvFactorials {
+  uint64_t q62[20];
+  double dbl[20];
+  constexpr InvFactorials() : q62{}, dbl{} {
+    uint64_t f = 1;
+    for (int j = 0; j < 20; ++j) {
+      if (j > 1) f *= (uint64_t)j;
+      q62[j] = ((1ull << 62) + f / 2) / f;
+      dbl[j] = 1.0 / (double)f;  // j! is exact in double for j <= 18; 1/j! rounded once
+    }
+  }
+};
+constexpr InvFactorials kInvFact{};
+
+__device__ __forceinline__ float cr_expf_exact(float L) {
   const float mag = __builtin_fabsf(L);
   if (!(mag <= 80.0f)) return L > 0.0f ? __builtin_inff() : (L < 0.0f ? 0.0f : L);  // outside the domain
   // |L| < 2^-30: e^L rounds to 1 (the nearest midpoints are 1 + 2^-24 and 1 - 2^-25).
@@ -99,112 +114,88 @@ __device__ __forceinline__ float cr_expf(float L) {
   __int128 lq = (__int128)mant << (biased - 54);
   if (bits >> 31) lq = -lq;
 
-  const __int128 kLn2Q96 = ((__int128)0xB17217F7ull << 64) | (__int128)0xD1CF79ABC9E3B398ull;
-  int k = (int)__builtin_floorf(L * 1.44269504f);  // estimate, fixed up below
-  __int128 r = lq - (__int128)k * kLn2Q96;
+  const __int128 step = ((__int128)kLn2Over32Q96Hi << 64) | (__int128)kLn2Over32Q96Lo;
+  int k = (int)__builtin_floorf(L * 46.1662413f);  // estimate of floor(L / step), fixed up below
+  __int128 r = lq - (__int128)k * step;
 #pragma unroll
   for (int fix = 0; fix < 2; ++fix) {
     if (r < 0) {
-      r += kLn2Q96;
+      r += step;
       --k;
-    } else if (r >= kLn2Q96) {
-      r -= kLn2Q96;
+    } else if (r >= step) {
+      r -= step;
       ++k;
     }
   }
-  const uint64_t r64 = (uint64_t)(r >> 32);  // r in Q64, r < ln 2
+  const uint64_t r64 = (uint64_t)(r >> 32);  // r in Q64, r < ln 2 / 32
 
-  uint64_t p = inv_factorial_q62(19);
+  uint64_t p = kInvFact.q62[8];
 #pragma unroll
-  for (int j = 18; j >= 0; --j) p = inv_factorial_q62(j) + __umul64hi(p, r64);
-  // p = e^r in Q62, in [2^62, 2^63): keep 24 bits, round to nearest even.
-  uint64_t m24 = p >> 39;
-  const uint64_t rest = p & ((1ull << 39) - 1);
-  const uint64_t half = 1ull << 38;
+  for (int j = 7; j >= 0; --j) p = kInvFact.q62[j] + __umul64hi(p, r64);
+  // m = 2^((k & 31)/32) * e^r in Q62, in [2^62, 2^64)
+  const uint64_t t = kExp2Q62[k & 31];
+  const uint64_t m = (__umul64hi(t, p) << 2) | ((t * p) >> 62);
+  int e = k >> 5;  // floor(k / 32)
+  int shift = 39;
+  if (m >> 63) {
+    shift = 40;
+    ++e;
+  }
+  uint64_t m24 = m >> shift;
+  const uint64_t rest = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
   if (rest > half || (rest == half && (m24 & 1))) ++m24;
   if (m24 == (1ull << 24)) {
     m24 >>= 1;
-    ++k;
+    ++e;
   }
-  return __uint_as_float(((uint32_t)(k + 127) << 23) | ((uint32_t)m24 & 0x7FFFFFu));
+  return __uint_as_float(((uint32_t)(e + 127) << 23) | ((uint32_t)m24 & 0x7FFFFFu));
 }
 
 // ---------------------------------------------------------------------------
-// Correctly rounded fp32 sqrt of a positive normal float, integer arithmetic:
-// the mantissa is scaled to M in [2^48, 2^50) with an even exponent, q =
-// floor(sqrt(M)) has exactly 25 bits; the 25th bit is the rounding bit (an
-// exact tie is impossible for a square root).
+// Correctly rounded fp32 exp, fast path first (the usual scheme for correct
+// rounding: a cheap approximation with a proven error bound, and the exact
+// evaluation only when that bound cannot decide the rounding).  The fast
+// path touches no memory (a table lookup would cost a memory latency at the
+// start of every work-group).
+//   In double: k = round(L / ln 2), r = L - k ln 2 by a Cody-Waite pair
+//   (k*hi is exact for |k| < 2^11 and so is L - k*hi; the low term adds at
+//   most 2^-56 relative), |r| <= 0.35, e^r by its degree-14 Taylor polynomial
+//   (tail below 2^-57), scaled by 2^k.  Relative error below 3 units of
+//   2^-53 < 2^-50.
+//   The result y rounds to f; if no fp32 rounding midpoint lies within
+//   y * 2^-50 of y, the true value rounds to f as well.  Otherwise (about
+//   one argument in 2^25) the exact fixed-point evaluation above decides.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t isqrt_u50(uint64_t M) {
-  uint64_t q = (uint64_t)__builtin_sqrt((double)M);  // estimate; M < 2^53 converts exactly
+__device__ __forceinline__ float cr_expf(float L) {
+  const float mag = __builtin_fabsf(L);
+  if (!(mag <= 80.0f) || !(mag >= 0x1p-30f)) return cr_expf_exact(L);
+  const double x = (double)L;
+  const double kd = __builtin_rint(x * 1.4426950408889634);  // 1 / ln 2
+  double r = __builtin_fma(-kd, kLn2Hi, x);
+  r = __builtin_fma(-kd, kLn2Lo, r);
+  double p = kInvFact.dbl[14];
 #pragma unroll
-  for (int fix = 0; fix < 3; ++fix) {
-    if (q * q > M) --q;
-  }
-#pragma unroll
-  for (int fix = 0; fix < 3; ++fix) {
-    if ((q + 1) * (q + 1) <= M) ++q;
-  }
-  return q;
+  for (int j = 13; j >= 0; --j) p = __builtin_fma(p, r, kInvFact.dbl[j]);
+  const double y = __builtin_ldexp(p, (int)kd);
+  const float f = (float)y;  // nearest even
+  const uint32_t fb = __float_as_uint(f);
+  const double ulp = __builtin_ldexp(1.0, (int)((fb >> 23) & 0xFFu) - 150);
+  double mid;
+  if (y >= (double)f)
+    mid = (double)f + 0.5 * ulp;
+  else
+    mid = (double)f - ((fb & 0x7FFFFFu) == 0 ? 0.25 : 0.5) * ulp;  // spacing halves below a power of 2
+  const double dist = __builtin_fabs(y - mid);
+  if (dist > y * 0x1p-50) return f;
+  return cr_expf_exact(L);
 }
 
-__device__ __forceinline__ float cr_sqrtf(float x) {
-  const uint32_t bits = __float_as_uint(x);
-  const int e = (int)(bits >> 23) - 150;  // x = m * 2^e
-  const uint64_t m = (bits & 0x7FFFFFu) | 0x800000u;
-  uint64_t M;
-  int f;  // sqrt(x) = sqrt(M) * 2^f
-  if (e & 1) {
-    M = m << 25;
-    f = (e - 25) / 2;
-  } else {
-    M = m << 26;
-    f = (e - 26) / 2;
-  }
-  const uint64_t q = isqrt_u50(M);  // [2^24, 2^25)
-  uint32_t mant = (uint32_t)(q >> 1);
-  int exp2 = f + 1;                 // value = mant * 2^exp2
-  if (q & 1) ++mant;
-  if (mant == (1u << 24)) {
-    mant >>= 1;
-    ++exp2;
-  }
-  return __uint_as_float(((uint32_t)(exp2 + 23 + 127) << 23) | (mant & 0x7FFFFFu));
-}
-
-// ---------------------------------------------------------------------------
-// Correctly rounded fp32 a / b for positive normal a, b with a normal
-// quotient, integer long division of the mantissas (an exact tie is
-// impossible for a quotient of two floats).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float cr_divf(float a, float b) {
-  const uint32_t ab = __float_as_uint(a), bb = __float_as_uint(b);
-  const int ea = (int)(ab >> 23), eb = (int)(bb >> 23);
-  const uint64_t ma = (ab & 0x7FFFFFu) | 0x800000u, mb = (bb & 0x7FFFFFu) | 0x800000u;
-  const uint64_t num = ma << 26;
-  const uint64_t Q = num / mb;
-  const bool inexact = (num - Q * mb) != 0;
-  uint32_t mant;
-  bool round_bit, sticky;
-  int biased;
-  if (Q >= (1ull << 26)) {  // 27 bits
-    mant = (uint32_t)(Q >> 3);
-    round_bit = (Q >> 2) & 1;
-    sticky = (Q & 3) != 0 || inexact;
-    biased = ea - eb + 127;
-  } else {  // 26 bits
-    mant = (uint32_t)(Q >> 2);
-    round_bit = (Q >> 1) & 1;
-    sticky = (Q & 1) != 0 || inexact;
-    biased = ea - eb + 126;
-  }
-  if (round_bit && (sticky || (mant & 1))) ++mant;
-  if (mant == (1u << 24)) {
-    mant >>= 1;
-    ++biased;
-  }
-  return __uint_as_float(((uint32_t)biased << 23) | (mant & 0x7FFFFFu));
-}
+// Correctly rounded fp32 square root and division: the compiler's IEEE
+// sequences for sqrtf and '/' (the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt and without fast-math flags).
+__device__ __forceinline__ float cr_sqrtf(float x) { return __builtin_sqrtf(x); }
+__device__ __forceinline__ float cr_divf(float a, float b) { return a / b; }
 
 // Round half away from zero of a non-negative float, as an integer; values
 // at or beyond 2^31 come back as INT32_MAX (never accepted as a side; below
@@ -267,62 +258,81 @@ __device__ __forceinline__ uint32_t pick_word(const Block4& lo, const Block4& hi
 }
 
 // ---------------------------------------------------------------------------
-// The decisions of sample n, computed by one whole wavefront (all 64 lanes
-// must call it together; every lane gets the result).
+// The decisions of one sample, computed by a group of 16 lanes (lanes
+// 16g .. 16g+15 of a wavefront draw for the sample their caller passes; a
+// wavefront serves four samples at once).  Every lane of the wavefront must
+// make the call together; each lane gets its group's result.
 //
 // The stream is consumed in a fixed order, so the words of attempt a sit at
 // a known offset: flip word (if any), gate word, then two words per attempt,
-// then two for the corner.  Lane a < 10 evaluates attempt a and the corner
-// it would draw, all ten in parallel; the first lane whose rectangle fits is
-// the accepted attempt -- the same result as trying them one after another.
+// then two for the corner.  Lane a < 10 of a group evaluates attempt a and
+// the corner it would draw, all ten in parallel; the first lane whose
+// rectangle fits is the accepted attempt -- the same result as trying the
+// attempts one after another.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ SampleParams draw_sample_params(const DrawArgs& a, uint64_t n) {
+__device__ __forceinline__ SampleParams draw_sample_params16(const DrawArgs& a, uint64_t n) {
   const int lane = (int)(threadIdx.x & 63u);
+  const int leader = lane & ~15;           // first lane of this group
+  const int gl = lane & 15;
   const int has_flip = a.flip_p > 0.0f ? 1 : 0;
   const int has_gate = a.erase_p > 0.0f ? 1 : 0;
-  const int first_attempt_word = has_flip + 1;  // the flip word, then the gate word
+  const int first_attempt_word = has_flip + 1;  // after the flip word and the gate word
 
-  const int att = lane < 10 ? lane : 9;
-  const int kbase = first_attempt_word + 2 * att;  // area, ratio, row, column words
-  const int blk = kbase >> 2;
-  const Block4 lo = stream_block(a.seed, n, (uint64_t)blk);
-  const Block4 hi = stream_block(a.seed, n, (uint64_t)blk + 1);
-  const int o = kbase & 3;
-  const uint32_t w_scale = pick_word(lo, hi, o);
-  const uint32_t w_ratio = pick_word(lo, hi, o + 1);
-  const uint32_t w_row = pick_word(lo, hi, o + 2);
-  const uint32_t w_col = pick_word(lo, hi, o + 3);
-
-  const Attempt t = erase_attempt(a, w_scale, w_ratio);
-  const int32_t ci = t.fits ? word_randint(0, a.H - t.eh, w_row) : 0;
-  const int32_t cj = t.fits ? word_randint(0, a.W - t.ew, w_col) : 0;
-
-  // The flip and gate words are words 0 and 1 of block 0, which lane 0 holds
-  // (its first attempt word is word 1 or 2).
-  const uint32_t w0 = __shfl(lo.w[0], 0);
-  const uint32_t w1 = __shfl(lo.w[1], 0);
-  const uint32_t w_flip = w0;
+  // A sample uses at most 24 words (blocks 0..5): lane j of the group
+  // computes block min(j, 5), and lanes fetch the words they need from the
+  // lanes that hold them.
+  const Block4 own = stream_block(a.seed, n, (uint64_t)min(gl, 5));
+  // The flip and gate words are words 0 and 1, in the leader's block 0.
+  const uint32_t w0 = __shfl(own.w[0], leader);
+  const uint32_t w1 = __shfl(own.w[1], leader);
   const uint32_t w_gate = has_flip ? w1 : w0;
 
+  Attempt t{0, 0, false};
+  int32_t ci = 0, cj = 0;
+  if (has_gate) {  // the same for every lane: no attempt is drawn when erasing is off
+    // lane a < 10 evaluates attempt a (lanes 10..15 repeat attempt 9): its
+    // area, ratio, row and column words k .. k+3 lie in blocks k/4, k/4 + 1
+    const int att = min(gl, 9);
+    const int kbase = first_attempt_word + 2 * att;
+    const int src = leader + (kbase >> 2);
+    Block4 lo, hi;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      lo.w[c] = __shfl(own.w[c], src);
+      hi.w[c] = __shfl(own.w[c], min(src + 1, leader + 5));
+    }
+    const int o = kbase & 3;
+    const uint32_t w_scale = pick_word(lo, hi, o);
+    const uint32_t w_ratio = pick_word(lo, hi, o + 1);
+    const uint32_t w_row = pick_word(lo, hi, o + 2);
+    const uint32_t w_col = pick_word(lo, hi, o + 3);
+    t = erase_attempt(a, w_scale, w_ratio);
+    ci = t.fits ? word_randint(0, a.H - t.eh, w_row) : 0;
+    cj = t.fits ? word_randint(0, a.W - t.ew, w_col) : 0;
+  }
+
+  const uint64_t fits_all = __ballot(t.fits && (lane & 15) < 10);
+  const uint32_t fits = (uint32_t)(fits_all >> leader) & 0xFFFFu;
+  const int win = leader + (fits ? __builtin_ctz(fits) : 0);
+  const int32_t win_eh = __shfl(t.eh, win), win_ew = __shfl(t.ew, win);
+  const int32_t win_i = __shfl(ci, win), win_j = __shfl(cj, win);
+
   SampleParams p{};
-  p.flip = has_flip ? (word_to_unit(w_flip) < a.flip_p ? 1 : 0) : 0;
+  p.flip = has_flip ? (word_to_unit(w0) < a.flip_p ? 1 : 0) : 0;
   p.attempt = -1;
   p.words_used = has_flip + has_gate;
   const bool tried = has_gate && word_to_unit(w_gate) < a.erase_p;
-  const uint64_t fits = __ballot(t.fits && lane < 10);
-  if (tried) {
-    if (fits != 0) {
-      const int win = __builtin_ctzll(fits);
-      p.erase = 1;
-      p.attempt = win;
-      p.eh = __shfl(t.eh, win);
-      p.ew = __shfl(t.ew, win);
-      p.i = __shfl(ci, win);
-      p.j = __shfl(cj, win);
-      p.words_used += 2 * (win + 1) + 2;
-    } else {
-      p.words_used += 20;
-    }
+  if (tried && fits) {
+    const int a_star = win - leader;
+    p.erase = 1;
+    p.attempt = a_star;
+    p.eh = win_eh;
+    p.ew = win_ew;
+    p.i = win_i;
+    p.j = win_j;
+    p.words_used += 2 * (a_star + 1) + 2;
+  } else if (tried) {
+    p.words_used += 20;
   }
   return p;
 }

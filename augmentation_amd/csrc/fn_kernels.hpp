@@ -1,16 +1,23 @@
 // fn_kernels.hpp -- the GPU kernels of libfn.so (gfx950, wave64).
 //
-//   params_kernel        one wavefront per sample: the sample's decisions.
-//   fused_kernel         the one-pass operation (page "(11)
-//                        FusedNormalization", section 5): per work-group a
-//                        tile of whole rows of one image; wave 0 draws the
-//                        image's decisions, then every element is read from
-//                        the mirrored or original column, normalized with one
-//                        fma, zeroed inside the rectangle, and stored as fp32
-//                        or round-to-nearest-even fp16.
+//   params_kernel          four samples per wavefront: each sample's decisions.
+//   fused_grouped_kernel   the one-pass operation (page "(11)
+//                          FusedNormalization", section 5) for images whose
+//                          width is a multiple of the pixel group PX: each
+//                          lane owns groups of PX consecutive pixels of one
+//                          row.  A flipped group reads the mirrored group of
+//                          the same row (also PX contiguous pixels) and
+//                          reverses the pixel order in registers, keeping
+//                          the channel order; a group wholly inside the erase
+//                          rectangle reads nothing; values are one fma each
+//                          and are stored as fp32 or round-to-nearest-even
+//                          fp16 in 16-byte vectors.
+//   fused_generic_kernel   the same operation for any shape and alignment,
+//                          one element at a time (used when the grouped
+//                          kernel's shape or alignment conditions fail).
 //   erase_dims_kernel,
 //   cr_ops_kernel,
-//   copy_kernel          test and measurement hooks.
+//   copy_kernel            test and measurement hooks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,26 +27,100 @@
 
 namespace fn {
 
-constexpr int kBlock = 256;  // four wave64 wavefronts
+// Build-time tuning of the grouped kernel (defaults chosen by measurement):
+//   FN_GROUP_PX_MAX  widest pixel group tried (16, 8 or 4)
+//   FN_GROUP_ITER    pixel groups per lane (1..4)
+//   FN_NT_STORE      output stores: 0 default, 1 non-temporal, 2 streaming
+//                    system-scope (sc0 sc1 nt)
+#ifndef FN_GROUP_PX_MAX
+#define FN_GROUP_PX_MAX 16
+#endif
+#ifndef FN_GROUP_ITER
+#define FN_GROUP_ITER 4
+#endif
+#ifndef FN_NT_STORE
+#define FN_NT_STORE 1
+#endif
+
+#ifndef FN_TILE_BYTES
+#define FN_TILE_BYTES 16384
+#endif
+#ifndef FN_WG_PER_CU
+#define FN_WG_PER_CU 3  // 0: no cap, one tile per work-group
+#endif
+
+constexpr int kBlock = 256;             // four wave64 wavefronts
+constexpr int kTileBytesTarget = FN_TILE_BYTES;  // input bytes of one tile
+constexpr int kWgPerCu = FN_WG_PER_CU;           // rows-kernel work-groups per compute unit
+constexpr int kMinTilesPerCu = 2;                // smaller tiles when a batch gives fewer
+constexpr int kTileBytesMax = 16384;    // largest tile the rows kernel stages in LDS
+constexpr int kRowsBlock = 512;         // rows kernel: one producer + seven consumer wavefronts
+constexpr int kMaxImagesPerBlock = 16;  // images whose decisions one work-group draws
+constexpr int kMaxIter = FN_GROUP_ITER;  // pixel groups per lane in the grouped kernel
+constexpr int kGroupPxMax = FN_GROUP_PX_MAX;
+
+// Division of 32-bit x by a fixed d >= 1 through a multiply-high and one
+// correction (valid for x + d < 2^32): m = floor(2^32 / d) + 1 overestimates
+// 1/d by less than 1/2^32, so mulhi(x, m) is x/d or x/d + 1.
+struct FastDiv {
+  uint32_t d, m;
+};
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t x, FastDiv f) {
+  if (f.d == 1) return x;
+  uint32_t q = __umulhi(x, f.m);
+  if (q * f.d > x) --q;
+  return q;
+}
 
 struct FusedArgs {
   const uint8_t* in;
   void* out;
   int64_t N;
   int32_t H, W, C;
+  // generic kernel: tiles of whole rows
   int32_t rows_per_tile, tiles_per_image;
-  float mul[4];  // RN32(1 / (255 std_c))
-  float sub[4];  // RN32(mean_c / std_c)
+  // grouped kernel
+  int64_t total_groups;       // N * H * W / PX
+  uint32_t groups_per_image;  // H * W / PX
+  uint32_t groups_per_row;    // W / PX
+  FastDiv div_gpi, div_gpr;
+  int32_t iter;               // groups per lane, 1..kMaxIter
+  // rows kernel: a tile is rows_per_tile rows of one image, or
+  // images_per_tile whole images
+  int32_t images_per_tile;
+  int64_t total_tiles;
+  int32_t lds_buffer_bytes;   // one of the two LDS staging buffers
+  int64_t total_bytes;        // N * H * W * C
+  FastDiv div_row;            // by W * C
+  FastDiv div_h;              // by H
+  float mul[4];               // RN32(1 / (255 std_c))
+  float nsub[4];              // -RN32(mean_c / std_c)
   DrawArgs draw;
 };
 
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kBlock) params_kernel(DrawArgs a, int64_t N,
                                                         SampleParams* __restrict__ out) {
-  const int64_t n = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  if (n >= N) return;  // whole wavefronts leave together
-  const SampleParams p = draw_sample_params(a, (uint64_t)n);
-  if ((threadIdx.x & 63u) == 0) out[n] = p;
+  const int64_t first = (int64_t)blockIdx.x * (kBlock / 16);
+  if (first + (int64_t)(threadIdx.x >> 6) * 4 >= N) return;  // whole wavefronts leave together
+  const int64_t n = first + (threadIdx.x >> 4);
+  const SampleParams p = draw_sample_params16(a, (uint64_t)n);
+  if ((threadIdx.x & 15u) == 0 && n < N) out[n] = p;
+}
+
+// ---------------------------------------------------------------------------
+// Draws the decisions of images n_first .. n_first + count - 1 (count <= 16)
+// into s_params, 16 lanes per image; wavefronts with nothing to draw skip.
+__device__ __forceinline__ void draw_block_params(const DrawArgs& a, int64_t n_first, int count,
+                                                  SampleParams* s_params) {
+  const int wave = (int)(threadIdx.x >> 6);
+  if (wave * 4 < count) {
+    const int slot = (int)(threadIdx.x >> 4);
+    const SampleParams p = draw_sample_params16(a, (uint64_t)(n_first + slot));
+    if ((threadIdx.x & 15u) == 0 && slot < count) s_params[slot] = p;
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -54,17 +135,470 @@ __device__ __forceinline__ _Float16 to_out<_Float16>(float v) {
   return (_Float16)v;  // v_cvt_f16_f32: round to nearest even
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int NB>
+__device__ __forceinline__ void load_group(const uint8_t* __restrict__ p, uint32_t (&w)[NB / 4]) {
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int v = 0; v < NB / 16; ++v) {
+      const uint4 q = reinterpret_cast<const uint4*>(p)[v];
+      w[4 * v] = q.x;
+      w[4 * v + 1] = q.y;
+      w[4 * v + 2] = q.z;
+      w[4 * v + 3] = q.w;
+    }
+  } else if constexpr (NB % 8 == 0) {
+#pragma unroll
+    for (int v = 0; v < NB / 8; ++v) {
+      const uint2 q = reinterpret_cast<const uint2*>(p)[v];
+      w[2 * v] = q.x;
+      w[2 * v + 1] = q.y;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < NB / 4; ++v) w[v] = reinterpret_cast<const uint32_t*>(p)[v];
+  }
+}
+
+// Stores NE output values as 16-, 8- or 4-byte vectors.
+template <typename OutT, int NE>
+__device__ __forceinline__ void store_group(OutT* __restrict__ dst, const float (&v)[NE]) {
+  constexpr int kBytes = NE * (int)sizeof(OutT);
+  constexpr int kWords = kBytes / 4;
+  uint32_t u[kWords];
+  if constexpr (sizeof(OutT) == 4) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) u[e] = __float_as_uint(v[e]);
+  } else {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < NE; e += 2) {
+      const half2_t h = {to_out<_Float16>(v[e]), to_out<_Float16>(v[e + 1])};
+      u[e / 2] = __builtin_bit_cast(uint32_t, h);
+    }
+  }
+  if constexpr (kBytes % 16 == 0) {
+#pragma unroll
+    for (int s = 0; s < kWords / 4; ++s) {
+      const u32x4 q = {u[4 * s], u[4 * s + 1], u[4 * s + 2], u[4 * s + 3]};
+      u32x4* p = reinterpret_cast<u32x4*>(dst) + s;
+      if constexpr (FN_NT_STORE == 1) {
+        __builtin_nontemporal_store(q, p);
+      } else if constexpr (FN_NT_STORE == 2) {
+        asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(p), "v"(q) : "memory");
+      } else {
+        *p = q;
+      }
+    }
+  } else if constexpr (kBytes % 8 == 0) {
+#pragma unroll
+    for (int s = 0; s < kWords / 2; ++s)
+      reinterpret_cast<uint2*>(dst)[s] = make_uint2(u[2 * s], u[2 * s + 1]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < kWords; ++s) reinterpret_cast<uint32_t*>(dst)[s] = u[s];
+  }
+}
+
+// One group's outputs from its (possibly mirrored) source bytes: pixel p of
+// the output takes pixel PX-1-p of the source when flipped, channels in
+// order; pixels whose bit is set in `erased` are +0.
+template <int C, int PX, bool kFlip, bool kMasked>
+__device__ __forceinline__ void group_values(const uint32_t (&w)[PX * C / 4], uint32_t erased,
+                                             const FusedArgs& a, float (&v)[PX * C]) {
+  constexpr int NW = PX * C / 4;
+#pragma unroll
+  for (int p = 0; p < PX; ++p) {
+    const int sp = kFlip ? (PX - 1 - p) : p;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float x;
+      switch (((sp * C + c) & 3)) {  // resolved at compile time
+        case 0: x = (float)(w[(sp * C + c) >> 2] & 0xFFu); break;
+        case 1: x = (float)((w[(sp * C + c) >> 2] >> 8) & 0xFFu); break;
+        case 2: x = (float)((w[(sp * C + c) >> 2] >> 16) & 0xFFu); break;
+        default: x = (float)(w[(sp * C + c) >> 2] >> 24); break;
+      }
+      float y = __builtin_fmaf(x, a.mul[c], a.nsub[c]);
+      if (kMasked) y = ((erased >> p) & 1u) ? 0.0f : y;
+      v[p * C + c] = y;
+    }
+  }
+  (void)NW;
+}
+
+template <int C, int PX, typename OutT>
+__global__ void __launch_bounds__(kBlock) fused_grouped_kernel(FusedArgs a) {
+  constexpr int NB = PX * C;  // input bytes (= output elements) per group
+  constexpr uint32_t kAll = (PX >= 32) ? 0xFFFFFFFFu : ((1u << PX) - 1u);
+  __shared__ SampleParams s_params[kMaxImagesPerBlock];
+
+  const int64_t per_block = (int64_t)kBlock * a.iter;
+  const int64_t g_begin = (int64_t)blockIdx.x * per_block;
+  const int64_t g_end = min(g_begin + per_block, a.total_groups);
+  const int64_t n_first = g_begin / a.groups_per_image;
+  const int n_count = (int)((g_end - 1) / a.groups_per_image - n_first + 1);
+  draw_block_params(a.draw, n_first, n_count, s_params);
+
+  const uint32_t local0 = (uint32_t)(g_begin - n_first * (int64_t)a.groups_per_image);
+  uint32_t words[kMaxIter][NB / 4];
+  uint32_t erased[kMaxIter];
+  int32_t flip[kMaxIter];
+#pragma unroll
+  for (int k = 0; k < kMaxIter; ++k) {
+    erased[k] = kAll;
+    flip[k] = 0;
+    const int64_t g = g_begin + threadIdx.x + (int64_t)k * kBlock;
+    if (k < a.iter && g < g_end) {
+      const uint32_t local = local0 + threadIdx.x + (uint32_t)k * kBlock;
+      const uint32_t img = fast_div(local, a.div_gpi);
+      const uint32_t rem = local - img * a.groups_per_image;
+      const uint32_t h = fast_div(rem, a.div_gpr);
+      const uint32_t wg = rem - h * a.groups_per_row;  // group index within the row
+      const SampleParams& P = s_params[img];
+      uint32_t m = 0;
+      if (P.erase && (int32_t)h >= P.i && (int32_t)h < P.i + P.eh) {
+        const int32_t px0 = (int32_t)wg * PX;
+        const int32_t lo = max(P.j - px0, 0), hi = min(P.j + P.ew - px0, PX);
+        if (lo < hi) m = (kAll >> (PX - (hi - lo))) << lo;
+      }
+      erased[k] = m;
+      flip[k] = P.flip;
+      if (m != kAll) {
+        const int64_t src = P.flip ? g + (int64_t)a.groups_per_row - 1 - 2 * (int64_t)wg : g;
+        load_group<NB>(a.in + src * NB, words[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxIter; ++k) {
+    const int64_t g = g_begin + threadIdx.x + (int64_t)k * kBlock;
+    if (k < a.iter && g < g_end) {
+      float v[NB];
+      if (erased[k] == kAll) {
+#pragma unroll
+        for (int e = 0; e < NB; ++e) v[e] = 0.0f;
+      } else if (erased[k] == 0) {
+        if (flip[k])
+          group_values<C, PX, true, false>(words[k], 0, a, v);
+        else
+          group_values<C, PX, false, false>(words[k], 0, a, v);
+      } else {
+        if (flip[k])
+          group_values<C, PX, true, true>(words[k], erased[k], a, v);
+        else
+          group_values<C, PX, false, true>(words[k], erased[k], a, v);
+      }
+      store_group<OutT, NB>(reinterpret_cast<OutT*>(a.out) + g * NB, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiles of the rows kernel: a tile is a run of whole rows -- rows_per_tile
+// rows of one image (images_per_tile == 1), or images_per_tile whole images.
+struct Tile {
+  int64_t n_first;  // first image
+  int32_t h0;       // first row in that image
+  int32_t rows;     // rows in the tile (across images when several)
+  int64_t start;    // first input byte / output element
+  int32_t len;      // input bytes = output elements
+};
+
+__device__ __forceinline__ Tile tile_at(const FusedArgs& a, int64_t t) {
+  Tile T;
+  const int32_t row = a.W * a.C;
+  if (a.images_per_tile == 1) {
+    T.n_first = t / a.tiles_per_image;
+    T.h0 = (int32_t)(t - T.n_first * a.tiles_per_image) * a.rows_per_tile;
+    T.rows = min(a.rows_per_tile, a.H - T.h0);
+  } else {
+    T.n_first = t * a.images_per_tile;
+    T.h0 = 0;
+    T.rows = (int32_t)min((int64_t)a.images_per_tile, a.N - T.n_first) * a.H;
+  }
+  T.start = (T.n_first * a.H + T.h0) * (int64_t)row;
+  T.len = T.rows * row;
+  return T;
+}
+
+// Image index (into s_params, relative to n_base) and image row of tile row r.
+__device__ __forceinline__ void tile_row_image(const FusedArgs& a, const Tile& T, int64_t n_base,
+                                               int32_t r, uint32_t* slot, int32_t* h) {
+  if (a.images_per_tile == 1) {
+    *slot = (uint32_t)(T.n_first - n_base);
+    *h = T.h0 + r;
+  } else {
+    const uint32_t img = fast_div((uint32_t)r, a.div_h);
+    *slot = (uint32_t)(T.n_first - n_base) + img;
+    *h = r - (int32_t)img * a.H;
+  }
+}
+
+// Producer side: moves tile T's input bytes into the LDS buffer `buf` (byte
+// b of the tile at buf[head + b], head = the tile start's offset within its
+// 16-byte granule).  One wavefront issues the granules 64 at a time as
+// global-to-LDS DMA loads (lane l of a batch lands at 16*l past the batch's
+// base).  With `skip`, a granule whose tile bytes all lie in an erased
+// source region is not read.  Granules that straddle the ends of the input
+// buffer are read byte by byte, so nothing outside it is read.  The caller
+// waits for the loads (vmcnt) before releasing the buffer to consumers.
+template <int C>
+__device__ __forceinline__ int32_t issue_tile(const FusedArgs& a, const Tile& T, int64_t n_base,
+                                              const SampleParams* s_params, bool skip,
+                                              uint8_t* buf) {
+  const int32_t row = a.W * C;
+  const int lane = (int)(threadIdx.x & 63u);
+  const uintptr_t in_lo = (uintptr_t)a.in, in_hi = in_lo + (uintptr_t)a.total_bytes;
+  const uintptr_t t_lo = in_lo + (uintptr_t)T.start;
+  const uintptr_t gbase = t_lo & ~(uintptr_t)15;
+  const int32_t head = (int32_t)(t_lo - gbase);
+  const int32_t ngran = (head + T.len + 15) >> 4;
+  // Single-image tile: the erased source block is rows [er0, er1) of the
+  // tile, bytes [se0, se1) of each of those rows (empty when not erasing).
+  int32_t er0 = 0, er1 = 0, se0 = 0, se1 = 0;
+  const bool single = a.images_per_tile == 1;
+  if (skip && single) {
+    const SampleParams& P = s_params[T.n_first - n_base];
+    if (P.erase) {
+      er0 = max(P.i - T.h0, 0);
+      er1 = min(P.i + P.eh - T.h0, T.rows);
+      se0 = (P.flip ? a.W - P.j - P.ew : P.j) * C;
+      se1 = se0 + P.ew * C;
+    }
+  }
+  const bool any_erased = er0 < er1 || (skip && !single);
+  for (int32_t batch = 0; batch < ngran; batch += 64) {
+    const int32_t g = batch + lane;
+    bool load = g < ngran;
+    if (load && any_erased) {
+      // tile bytes held by this granule: [b_lo, b_hi] (tile-relative, inclusive)
+      const int32_t b_lo = max(16 * g - head, 0);
+      const int32_t b_hi = min(16 * g + 15 - head, T.len - 1);
+      const uint32_t r_lo = fast_div((uint32_t)b_lo, a.div_row);
+      const uint32_t r_hi = fast_div((uint32_t)b_hi, a.div_row);
+      if (r_lo == r_hi) {
+        const int32_t x_lo = b_lo - (int32_t)r_lo * row;
+        const int32_t x_hi = b_hi - (int32_t)r_lo * row;
+        if (single) {
+          if ((int32_t)r_lo >= er0 && (int32_t)r_lo < er1 && x_lo >= se0 && x_hi < se1) load = false;
+        } else {
+          uint32_t slot;
+          int32_t h;
+          tile_row_image(a, T, n_base, (int32_t)r_lo, &slot, &h);
+          const SampleParams& P = s_params[slot];
+          if (P.erase && h >= P.i && h < P.i + P.eh) {
+            const int32_t s0 = (P.flip ? a.W - P.j - P.ew : P.j) * C;
+            if (x_lo >= s0 && x_hi < s0 + P.ew * C) load = false;
+          }
+        }
+      }
+    }
+    const uintptr_t A = gbase + 16 * (uintptr_t)g;
+    if (load && A >= in_lo && A + 16 <= in_hi) {
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(A),
+                                       (__attribute__((address_space(3))) void*)(buf + 16 * batch),
+                                       16, 0, 0);
+    } else if (load) {  // the buffer's first or last granule, not fully inside it
+      for (int b = 0; b < 16; ++b) {
+        const uintptr_t addr = A + (uintptr_t)b;
+        if (addr >= in_lo && addr < in_hi) buf[16 * g + b] = *reinterpret_cast<const uint8_t*>(addr);
+      }
+    }
+  }
+  return head;
+}
+
+// Work-group barrier that orders LDS only: the caller has already waited for
+// whatever must be complete (the producer's DMA loads); outstanding global
+// stores of the consumers are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
+// What one lane needs to turn the E elements of a row starting at element
+// x0 into outputs, independent of the row: the channel of each element and
+// its constants, and the byte offsets (from the row start) of its mirrored
+// sources.  Element x = w*C + c takes byte (W-1-w)*C + c when flipped; with
+// x0 = w0*C + c0 and rc_k = (c0 + k) mod C that byte is
+// (W-1-w0)*C - c0 - k + 2 rc_k.
+template <int C, int E>
+struct ChunkSetup {
+  int32_t x0;
+  float mul[C], nsub[C];  // rotated: element k uses index k % C
+  int32_t mirror[E];      // mirrored source byte of element k, from the row start
+
+  __device__ __forceinline__ ChunkSetup(const FusedArgs& a, int32_t first) : x0(first) {
+    const int32_t w0 = x0 / C;
+    const int32_t c0 = x0 - w0 * C;
+    int32_t rc[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      int32_t cj = c0 + j;
+      cj = cj >= C ? cj - C : cj;
+      rc[j] = cj;
+      float m = a.mul[0], s = a.nsub[0];
+#pragma unroll
+      for (int cc = 1; cc < C; ++cc) {
+        m = cj == cc ? a.mul[cc] : m;
+        s = cj == cc ? a.nsub[cc] : s;
+      }
+      mul[j] = m;
+      nsub[j] = s;
+    }
+    const int32_t base = (a.W - 1 - w0) * C - c0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) mirror[k] = base - k + 2 * rc[k % C];
+  }
+
+  // Outputs of this lane's E elements of one row (LDS row start `row_lds`,
+  // image row h, the image's decisions P).
+  __device__ __forceinline__ void values(const uint8_t* s_tile, int32_t row_lds,
+                                         const SampleParams& P, int32_t h, float (&v)[E]) const {
+    float x[E];
+    const int32_t src = row_lds + x0;
+    if (P.flip) {
+#pragma unroll
+      for (int k = 0; k < E; ++k) x[k] = (float)s_tile[row_lds + mirror[k]];
+    } else if ((src & 3) == 0) {
+      uint32_t wv[E / 4];
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) wv[q] = reinterpret_cast<const uint32_t*>(s_tile + src)[q];
+#pragma unroll
+      for (int k = 0; k < E; ++k) x[k] = (float)((wv[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+    } else {
+#pragma unroll
+      for (int k = 0; k < E; ++k) x[k] = (float)s_tile[src + k];
+    }
+#pragma unroll
+    for (int k = 0; k < E; ++k) v[k] = __builtin_fmaf(x[k], mul[k % C], nsub[k % C]);
+    if (P.erase && h >= P.i && h < P.i + P.eh) {
+      const int32_t lo = P.j * C - x0, hi = (P.j + P.ew) * C - x0;
+#pragma unroll
+      for (int k = 0; k < E; ++k) v[k] = (k >= lo && k < hi) ? 0.0f : v[k];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fused_rows_kernel: work-group b owns tiles [b*T/G, (b+1)*T/G) of the T
+// tiles (G work-groups), consecutive runs of whole rows.  Wavefront 0 is the
+// producer, the other seven are consumers; the two roles never share a
+// memory counter, so the producer waits only for its loads and the
+// consumers never wait for their stores.
+//   producer: DMA the first tile into LDS buffer 0 (no skipping: the
+//     decisions are being drawn meanwhile); then, while the consumers work
+//     on tile i, DMA tile i+1 into the other buffer, skipping wholly erased
+//     granules.
+//   consumers: draw the decisions of every image the range touches (16
+//     lanes per image, in parallel); then per tile, each lane makes
+//     E = 16/sizeof(OutT) consecutive output elements of a row and stores
+//     them as one 16-byte vector, lane-contiguous across the wavefront.
+//     Output element x of a row (x = w*C + c) takes source byte
+//     (W-1-w)*C + c of the same row when the image is flipped, byte x when
+//     not; inside the erase rectangle it is +0.
+//   One LDS barrier per tile hands a filled buffer to the consumers and the
+//   drained one back to the producer.
+// Requires W*C a multiple of E (chunks never cross rows) and a 16-byte
+// aligned output.
+template <int C, typename OutT>
+__global__ void __launch_bounds__(kRowsBlock) fused_rows_kernel(FusedArgs a) {
+  constexpr int E = 16 / (int)sizeof(OutT);
+  extern __shared__ __align__(16) uint8_t s_lds[];
+  __shared__ SampleParams s_params[kMaxImagesPerBlock];
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.total_tiles / gridDim.x;
+  const int64_t t_end = ((int64_t)blockIdx.x + 1) * a.total_tiles / gridDim.x;
+  if (t_begin >= t_end) return;  // whole work-group
+  const int32_t ntiles = (int32_t)(t_end - t_begin);
+  const Tile first = tile_at(a, t_begin);
+  const Tile last = tile_at(a, t_end - 1);
+  const int64_t n_base = first.n_first;
+  const int n_count = (int)(last.n_first + (last.rows - 1) / a.H - n_base + 1);
+  uint8_t* const buf0 = s_lds;
+  uint8_t* const buf1 = s_lds + a.lds_buffer_bytes;
+
+  if (threadIdx.x < 64) {
+    // ---------------- producer ----------------
+    issue_tile<C>(a, first, n_base, s_params, false, buf0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads have landed
+    lds_barrier();                  // decisions drawn, tile 0 staged
+    for (int32_t i = 0; i + 1 < ntiles; ++i) {
+      issue_tile<C>(a, tile_at(a, t_begin + i + 1), n_base, s_params, true, (i & 1) ? buf0 : buf1);
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
+    }
+    return;
+  }
+
+  // ---------------- consumers ----------------
+  const int ct = (int)threadIdx.x - 64;  // consumer thread, 0 .. kRowsBlock - 65
+  {
+    const int wave = ct >> 6;
+    if (wave * 4 < n_count) {
+      const int slot = ct >> 4;
+      const SampleParams p = draw_sample_params16(a.draw, (uint64_t)(n_base + slot));
+      if ((ct & 15) == 0 && slot < n_count) s_params[slot] = p;
+    }
+  }
+  lds_barrier();
+
+  const int32_t row = a.W * C;
+  const int32_t cpr = row / E;  // chunks per row
+  constexpr int kConsumers = kRowsBlock - 64;
+  const int32_t rpi = cpr <= kConsumers ? kConsumers / cpr : 0;  // rows per pass when a row fits
+  const int32_t slot_row = rpi ? ct / cpr : 0;
+  const bool active = rpi ? slot_row < rpi : true;
+  const ChunkSetup<C, E> cs(a, rpi ? (ct - slot_row * cpr) * E : 0);
+
+  for (int32_t i = 0; i < ntiles; ++i) {
+    const Tile T = tile_at(a, t_begin + i);
+    const uint8_t* buf = (i & 1) ? buf1 : buf0;
+    const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
+    OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + T.start;
+    if (rpi) {
+      if (active) {
+        for (int32_t r = slot_row; r < T.rows; r += rpi) {
+          uint32_t slot;
+          int32_t h;
+          tile_row_image(a, T, n_base, r, &slot, &h);
+          float v[E];
+          cs.values(buf, head + r * row, s_params[slot], h, v);
+          store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
+        }
+      }
+    } else {
+      // rows wider than one pass of the consumers: per-chunk setup
+      const int32_t nchunks = T.len / E;
+      for (int32_t q = ct; q < nchunks; q += kConsumers) {
+        const int32_t off = q * E;
+        const uint32_t r = fast_div((uint32_t)off, a.div_row);
+        const int32_t x0 = off - (int32_t)r * row;
+        uint32_t slot;
+        int32_t h;
+        tile_row_image(a, T, n_base, (int32_t)r, &slot, &h);
+        const ChunkSetup<C, E> cq(a, x0);
+        float v[E];
+        cq.values(buf, head + (int32_t)r * row, s_params[slot], h, v);
+        store_group<OutT, E>(out + off, v);
+      }
+    }
+    if (i + 1 < ntiles) lds_barrier();  // done with this buffer; the next one is staged
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <typename OutT>
-__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
-  __shared__ SampleParams s_params;
+__global__ void __launch_bounds__(kBlock) fused_generic_kernel(FusedArgs a) {
+  __shared__ SampleParams s_params[kMaxImagesPerBlock];
   const int64_t n = blockIdx.x / a.tiles_per_image;
   const int tile = (int)(blockIdx.x % a.tiles_per_image);
-  if (threadIdx.x < 64) {
-    const SampleParams p = draw_sample_params(a.draw, (uint64_t)n);
-    if (threadIdx.x == 0) s_params = p;
-  }
-  __syncthreads();
-  const SampleParams p = s_params;
+  draw_block_params(a.draw, n, 1, s_params);
+  const SampleParams p = s_params[0];
 
   const int32_t W = a.W, C = a.C;
   const int64_t row_elems = (int64_t)W * C;
@@ -85,7 +619,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     if (!erased) {
       const int32_t src_w = p.flip ? (W - 1 - w) : w;
       const uint8_t x = a.in[img_base + (int64_t)h * row_elems + (int64_t)src_w * C + c];
-      v = __builtin_fmaf((float)x, a.mul[c], -a.sub[c]);
+      v = __builtin_fmaf((float)x, a.mul[c], a.nsub[c]);
     }
     out[begin + idx] = to_out<OutT>(v);
   }

@@ -38,9 +38,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fused_kernel_imagenet_train_counters.txt")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fused_rows_kernel_imagenet_train_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "augmentation_amd", "csrc", f)
-                  for f in ("fn_api.hip", "fn_kernels.hpp", "fn_device.hpp")]
+                  for f in ("fn_api.hip", "fn_kernels.hpp", "fn_device.hpp", "exp2_table.inc")]
 
 
 def kernel_source_hash() -> str:

@@ -5,8 +5,12 @@ Bars (checked element by element on the same seeded inputs):
     bit-exact;
   - fp32 output: |gpu - oracle| <= 2e-6, erased elements exactly +0.0;
   - fp16 output: |gpu - oracle| <= one fp16 ulp at |oracle|, erased elements
-    exactly +0; and (informative, asserted loosely) nearly every element
-    equals the oracle rounded to nearest even.
+    exactly +0.  With the MNIST, CIFAR and ImageNet presets every fp16 output
+    also equals the oracle rounded to nearest even (an exhaustive check of
+    all 256 byte values per channel shows the fp32 fma never crosses an fp16
+    rounding midpoint there), so preset workloads assert that exactly; with
+    arbitrary constants the fma's rounding may move 1 ulp, which the bound
+    above allows.
 """
 from __future__ import annotations
 
@@ -43,8 +47,9 @@ def ulp16(ref: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(a)) - 10)
 
 
-def check_values(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
-    """Compare a GPU output (fp32 or fp16) with the oracle's fp32 result."""
+def check_values(got: np.ndarray, ref: np.ndarray, what: str, rne_exact: bool = True) -> dict:
+    """Compare a GPU output (fp32 or fp16) with the oracle's fp32 result.
+    rne_exact: fp16 must equal RNE16(oracle) everywhere (preset constants)."""
     assert got.shape == ref.shape, what
     zero = ref.view(np.uint32) == 0
     if got.dtype == np.float32:
@@ -58,7 +63,8 @@ def check_values(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
     assert not np.any(bad), (what, int(bad.sum()), float(err.max()))
     assert np.all(got.view(np.uint16)[zero] == 0), what
     same = float(np.mean(got.view(np.uint16) == ref.astype(np.float16).view(np.uint16)))
-    assert same >= 0.9999, (what, same)  # a round-toward-zero conversion would give ~0.5
+    if rne_exact:
+        assert same == 1.0, (what, same)
     return {"max_abs": float(err.max(initial=0.0)), "rne_equal": same}
 
 
@@ -147,12 +153,17 @@ def test_stress_eight_back_to_back_launches(b):
 
 EDGE_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1, 3),
                (1, 1, 17, 3), (5, 17, 1, 3), (3, 2, 2, 1), (2, 31, 33, 3), (7, 13, 11, 4),
-               (2, 4, 8192, 1), (1, 600, 6, 3), (9, 28, 28, 1), (64, 32, 32, 3)]
+               (2, 4, 8192, 1), (1, 600, 6, 3), (9, 28, 28, 1), (64, 32, 32, 3),
+               (2, 3, 1024, 3), (2, 5, 700, 4), (40, 8, 8, 2), (3, 64, 48, 3)]
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES)
 @pytest.mark.parametrize("out_dtype", [0, 1])
-def test_edge_shapes_misaligned_with_guards(b, shape, out_dtype):
+@pytest.mark.parametrize("out_aligned", [True, False])
+def test_edge_shapes_with_guards(b, shape, out_dtype, out_aligned):
+    """Odd shapes, the input at a byte offset in 1..7, the output either
+    16-byte aligned or only element aligned; guard bands around the output
+    must stay untouched."""
     N, H, W, C = shape
     rng = np.random.default_rng(sum(shape) + out_dtype)
     x = rng.integers(0, 256, size=shape, dtype=np.uint8)
@@ -162,13 +173,13 @@ def test_edge_shapes_misaligned_with_guards(b, shape, out_dtype):
     elems = N * H * W * C
     esz = 4 if out_dtype == 0 else 2
     in_off = 1 + (sum(shape) % 7)          # input at a byte offset in 1..7
-    out_off = 4096 + esz                   # output element-aligned, not 16-aligned
+    out_off = 4096 if out_aligned else 4096 + esz
     guard = 4096
-    say(f"edge: shape={shape} out_dtype={out_dtype} in_off={in_off}")
+    say(f"edge: shape={shape} out_dtype={out_dtype} in_off={in_off} out_off={out_off}")
     in_buf = torch.zeros(elems + in_off + 64, dtype=torch.uint8, device="cuda")
     in_buf[in_off:in_off + elems] = torch.from_numpy(x.reshape(-1)).cuda()
     out_buf = torch.full((out_off + elems * esz + guard,), 0xA5, dtype=torch.uint8, device="cuda")
-    seed = 1000 + N
+    seed = 1000 + N + out_off
     b.fn_fused_normalize(in_buf.data_ptr() + in_off, N, H, W, C, mean, std, kw["flip_p"],
                          kw["erase_p"], 0.02, 0.33, 0.3, 3.3, seed, out_dtype,
                          out_buf.data_ptr() + out_off)
@@ -177,7 +188,7 @@ def test_edge_shapes_misaligned_with_guards(b, shape, out_dtype):
     assert np.all(host[:out_off] == 0xA5) and np.all(host[out_off + elems * esz:] == 0xA5)
     got = host[out_off:out_off + elems * esz].view(np.float32 if out_dtype == 0 else np.float16)
     ref, _ = oracle.fused_normalize(x, mean, std, kw["flip_p"], kw["erase_p"], seed=seed)
-    check_values(got.reshape(shape), ref, str(shape))
+    check_values(got.reshape(shape), ref, str(shape), rne_exact=False)
 
 
 def test_largest_image(b):
