@@ -3,6 +3,7 @@
 // meaning, layouts and error behaviour are documented in include/fn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -15,9 +16,6 @@
 
 #define FN_EXPORT extern "C" __attribute__((visibility("default")))
 
-#ifndef FN_USE_GROUPED
-#define FN_USE_GROUPED 0
-#endif
 
 namespace {
 
@@ -135,45 +133,6 @@ int device_cu_count(int* cus) {
   return FN_OK;
 }
 
-// Most images a run of `tiles` consecutive tiles can touch.
-int64_t max_images_per_range(const fn::FusedArgs& a, int64_t tiles) {
-  if (a.images_per_tile > 1) return tiles * a.images_per_tile;
-  return (tiles + a.tiles_per_image - 1) / a.tiles_per_image + 1;
-}
-
-// Tile plan of the rows kernel: whole rows, about kTileBytesTarget input
-// bytes per tile, smaller when the batch is too small to give every compute
-// unit kWgPerCu tiles.  Sets the tile fields of `a`.
-int plan_rows_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elems, int cus) {
-  int64_t target = fn::kTileBytesTarget;
-  const int64_t want = (int64_t)cus * fn::kMinTilesPerCu;
-  if (elems / want < target) target = elems / want;
-  if (target < row) target = row;
-  const int64_t image_bytes = (int64_t)H * row;
-  int64_t tile_bytes;
-  if (image_bytes <= target) {
-    int64_t g = target / image_bytes;
-    if (g > fn::kMaxImagesPerBlock) g = fn::kMaxImagesPerBlock;
-    a->images_per_tile = (int32_t)g;
-    a->rows_per_tile = H;
-    a->tiles_per_image = 1;
-    a->total_tiles = (N + g - 1) / g;
-    tile_bytes = g * image_bytes;
-  } else {
-    int64_t r = target / row;
-    if (r < 1) r = 1;
-    if (r > H) r = H;
-    a->images_per_tile = 1;
-    a->rows_per_tile = (int32_t)r;
-    a->tiles_per_image = (int32_t)((H + r - 1) / r);
-    a->total_tiles = N * a->tiles_per_image;
-    tile_bytes = r * row;
-  }
-  if (tile_bytes > fn::kTileBytesMax) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
-  a->lds_buffer_bytes = (int32_t)((tile_bytes + 32 + 15) / 16 * 16);
-  return FN_OK;
-}
-
 fn::FastDiv make_fast_div(uint32_t d) {
   fn::FastDiv f;
   f.d = d;
@@ -220,22 +179,54 @@ void launch_grouped_px(const fn::FusedArgs& a, int C, int out_dtype, unsigned gr
 }
 
 template <int C>
-void launch_rows_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t lds,
-                   hipStream_t st) {
+void launch_tiles_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t lds,
+                    hipStream_t st) {
   if (out_dtype == FN_OUT_FP32)
-    fn::fused_rows_kernel<C, float><<<grid, fn::kRowsBlock, lds, st>>>(a);
+    fn::fused_tiles_kernel<C, float><<<grid, fn::tiles_threads<float>(), lds, st>>>(a);
   else
-    fn::fused_rows_kernel<C, _Float16><<<grid, fn::kRowsBlock, lds, st>>>(a);
+    fn::fused_tiles_kernel<C, _Float16><<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
 }
 
-void launch_rows(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
-                 hipStream_t st) {
+void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
+                  hipStream_t st) {
   switch (C) {
-    case 1: launch_rows_c<1>(a, out_dtype, grid, lds, st); break;
-    case 2: launch_rows_c<2>(a, out_dtype, grid, lds, st); break;
-    case 3: launch_rows_c<3>(a, out_dtype, grid, lds, st); break;
-    default: launch_rows_c<4>(a, out_dtype, grid, lds, st); break;
+    case 1: launch_tiles_c<1>(a, out_dtype, grid, lds, st); break;
+    case 2: launch_tiles_c<2>(a, out_dtype, grid, lds, st); break;
+    case 3: launch_tiles_c<3>(a, out_dtype, grid, lds, st); break;
+    default: launch_tiles_c<4>(a, out_dtype, grid, lds, st); break;
   }
+}
+
+// Tile plan of the tiles kernel: the largest tile of at most kTileBytesTarget
+// input bytes (whole rows, or whole images when one fits), shrunk -- down to
+// kMinTileBytes -- so that the batch gives every compute unit at least 8
+// tiles.  Sets the tile fields of `a`.
+int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elems, int cus) {
+  int64_t target = fn::kTileBytesTarget;
+  const int64_t want = (int64_t)cus * 8;
+  if (elems / want < target) target = std::max<int64_t>(elems / want, fn::kMinTileBytes);
+  if (target < row) target = row;
+  const int64_t image_bytes = (int64_t)H * row;
+  int64_t tile_bytes;
+  if (image_bytes <= target) {
+    const int64_t g = std::min<int64_t>(target / image_bytes, fn::kMaxImagesPerBlock);
+    a->images_per_tile = (int32_t)g;
+    a->rows_per_tile = H;
+    a->tiles_per_image = 1;
+    a->total_tiles = (N + g - 1) / g;
+    tile_bytes = g * image_bytes;
+  } else {
+    const int64_t r = std::max<int64_t>(1, std::min<int64_t>(H, target / row));
+    a->images_per_tile = 1;
+    a->rows_per_tile = (int32_t)r;
+    a->tiles_per_image = (int32_t)((H + r - 1) / r);
+    a->total_tiles = N * a->tiles_per_image;
+    tile_bytes = r * row;
+  }
+  if (tile_bytes > fn::kTileBytesMax) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
+  if (a->total_tiles > 0x7FFFFFFF) return fail(FN_EOVERFLOW, "grid size limit exceeded");
+  a->lds_buffer_bytes = (int32_t)((tile_bytes + 32 + 15) / 16 * 16);
+  return FN_OK;
 }
 
 void launch_grouped(const fn::FusedArgs& a, int C, int px, int out_dtype, unsigned grid,
@@ -333,26 +324,17 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
 
   hipStream_t st = (hipStream_t)stream;
   a.total_bytes = elems;
-  if (!FN_USE_GROUPED && (uintptr_t)out_dev % 16 == 0 && row % (16 / out_bytes) == 0 &&
+  if ((uintptr_t)out_dev % 16 == 0 && row % (16 / out_bytes) == 0 &&
       row <= fn::kTileBytesMax) {
     int cus = 0;
     rc = device_cu_count(&cus);
     if (rc) return rc;
-    rc = plan_rows_tiles(&a, N, H, row, elems, cus);
+    rc = plan_tiles(&a, N, H, row, elems, cus);
     if (rc) return rc;
-    int64_t cap = fn::kWgPerCu > 0 ? (int64_t)cus * fn::kWgPerCu : a.total_tiles;
-    if (cap > 0x7FFFFFFF) cap = 0x7FFFFFFF;
-    unsigned g = (unsigned)(a.total_tiles < cap ? a.total_tiles : cap);
-    // no work-group may touch more images than it has decision slots
-    while ((int64_t)g < a.total_tiles && max_images_per_range(a, (a.total_tiles + g - 1) / g) >
-                                    fn::kMaxImagesPerBlock)
-      g = (unsigned)((int64_t)g * 2 > a.total_tiles ? a.total_tiles : (int64_t)g * 2);
-    if (max_images_per_range(a, (a.total_tiles + g - 1) / g) > fn::kMaxImagesPerBlock)
-      return fail(FN_EOVERFLOW, "tile plan exceeds the per-work-group image limit");
     a.div_row = make_fast_div((uint32_t)row);
     a.div_h = make_fast_div((uint32_t)H);
-    launch_rows(a, C, out_dtype, g, 2 * (size_t)a.lds_buffer_bytes, st);
-    return launch_status("fused_rows_kernel launch");
+    launch_tiles(a, C, out_dtype, (unsigned)a.total_tiles, (size_t)a.lds_buffer_bytes, st);
+    return launch_status("fused_tiles_kernel launch");
   }
   const int px = pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);
   if (px > 0) {

@@ -62,10 +62,11 @@ __device__ __forceinline__ float word_to_unit(uint32_t w) {
   return (float)(w >> 8) * 0x1p-24f;
 }
 
-// Inclusive randint(lo, hi) from one word, multiply-shift.
+// Inclusive randint(lo, hi) from one word, multiply-shift: lo plus the high
+// word of w * (hi - lo + 1).  Requires 0 <= hi - lo < 2^32 - 1.
 __device__ __forceinline__ int32_t word_randint(int32_t lo, int32_t hi, uint32_t w) {
-  const uint64_t span = (uint64_t)((int64_t)hi - (int64_t)lo + 1);
-  return lo + (int32_t)(((uint64_t)w * span) >> 32);
+  const uint32_t span = (uint32_t)(hi - lo) + 1u;
+  return lo + (int32_t)__umulhi(w, span);
 }
 
 // ---------------------------------------------------------------------------
@@ -257,65 +258,83 @@ __device__ __forceinline__ uint32_t pick_word(const Block4& lo, const Block4& hi
   return v;
 }
 
+// Lane i of a 16-lane row reads `x` from lane i + 2 of the same row (a DPP
+// row shift; lanes 14 and 15 keep their own value).
+__device__ __forceinline__ uint32_t from_lane_plus2(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x102 /* row_shl:2 */, 0xF, 0xF,
+                                               false);
+}
+
 // ---------------------------------------------------------------------------
 // The decisions of one sample, computed by a group of 16 lanes (lanes
 // 16g .. 16g+15 of a wavefront draw for the sample their caller passes; a
 // wavefront serves four samples at once).  Every lane of the wavefront must
-// make the call together; each lane gets its group's result.
+// make the call together; the group's first lane (16g) gets the result, the
+// other lanes' results are unspecified.
 //
 // The stream is consumed in a fixed order, so the words of attempt a sit at
 // a known offset: flip word (if any), gate word, then two words per attempt,
 // then two for the corner.  Lane a < 10 of a group evaluates attempt a and
 // the corner it would draw, all ten in parallel; the first lane whose
 // rectangle fits is the accepted attempt -- the same result as trying the
-// attempts one after another.
+// attempts one after another.  Attempt a reads words k .. k+3, k = f + 2a
+// (f = 1 + [flip drawn]), which lie in blocks k/4 and k/4 + 1: lane a
+// computes block k/4 itself and takes block k/4 + 1 from lane a + 2, which
+// computed exactly that block.  The flip and gate words are words 0 and 1,
+// in the first lane's own block 0.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ SampleParams draw_sample_params16(const DrawArgs& a, uint64_t n) {
   const int lane = (int)(threadIdx.x & 63u);
-  const int leader = lane & ~15;           // first lane of this group
   const int gl = lane & 15;
   const int has_flip = a.flip_p > 0.0f ? 1 : 0;
   const int has_gate = a.erase_p > 0.0f ? 1 : 0;
   const int first_attempt_word = has_flip + 1;  // after the flip word and the gate word
+  const int k = first_attempt_word + 2 * gl;
 
-  // A sample uses at most 24 words (blocks 0..5): lane j of the group
-  // computes block min(j, 5), and lanes fetch the words they need from the
-  // lanes that hold them.
-  const Block4 own = stream_block(a.seed, n, (uint64_t)min(gl, 5));
-  // The flip and gate words are words 0 and 1, in the leader's block 0.
-  const uint32_t w0 = __shfl(own.w[0], leader);
-  const uint32_t w1 = __shfl(own.w[1], leader);
-  const uint32_t w_gate = has_flip ? w1 : w0;
+  const Block4 own = stream_block(a.seed, n, (uint64_t)(k >> 2));
+  const uint32_t w0 = own.w[0];  // in the first lane: words 0 and 1 of the stream
+  const uint32_t w_gate = has_flip ? own.w[1] : own.w[0];
 
   Attempt t{0, 0, false};
   int32_t ci = 0, cj = 0;
   if (has_gate) {  // the same for every lane: no attempt is drawn when erasing is off
-    // lane a < 10 evaluates attempt a (lanes 10..15 repeat attempt 9): its
-    // area, ratio, row and column words k .. k+3 lie in blocks k/4, k/4 + 1
-    const int att = min(gl, 9);
-    const int kbase = first_attempt_word + 2 * att;
-    const int src = leader + (kbase >> 2);
-    Block4 lo, hi;
+    Block4 hi;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      lo.w[c] = __shfl(own.w[c], src);
-      hi.w[c] = __shfl(own.w[c], min(src + 1, leader + 5));
-    }
-    const int o = kbase & 3;
-    const uint32_t w_scale = pick_word(lo, hi, o);
-    const uint32_t w_ratio = pick_word(lo, hi, o + 1);
-    const uint32_t w_row = pick_word(lo, hi, o + 2);
-    const uint32_t w_col = pick_word(lo, hi, o + 3);
+    for (int c = 0; c < 4; ++c) hi.w[c] = from_lane_plus2(own.w[c]);
+    const int o = k & 3;
+    const uint32_t w_scale = pick_word(own, hi, o);
+    const uint32_t w_ratio = pick_word(own, hi, o + 1);
+    const uint32_t w_row = pick_word(own, hi, o + 2);
+    const uint32_t w_col = pick_word(own, hi, o + 3);
     t = erase_attempt(a, w_scale, w_ratio);
     ci = t.fits ? word_randint(0, a.H - t.eh, w_row) : 0;
     cj = t.fits ? word_randint(0, a.W - t.ew, w_col) : 0;
   }
 
-  const uint64_t fits_all = __ballot(t.fits && (lane & 15) < 10);
-  const uint32_t fits = (uint32_t)(fits_all >> leader) & 0xFFFFu;
-  const int win = leader + (fits ? __builtin_ctz(fits) : 0);
-  const int32_t win_eh = __shfl(t.eh, win), win_ew = __shfl(t.ew, win);
-  const int32_t win_i = __shfl(ci, win), win_j = __shfl(cj, win);
+  // first fitting attempt of each group, its values read into every lane of
+  // that group (the lane numbers are wavefront-uniform)
+  const uint64_t fits_all = __ballot(t.fits && gl < 10);
+  const int grp = lane >> 4;
+  uint32_t fits = 0;
+  int32_t win_eh = 0, win_ew = 0, win_i = 0, win_j = 0, a_star = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t fg = (uint32_t)(fits_all >> (16 * g)) & 0x3FFu;
+    const int ag = fg ? __builtin_ctz(fg) : 0;
+    const int src = 16 * g + ag;
+    const int32_t eh_g = __builtin_amdgcn_readlane(t.eh, src);
+    const int32_t ew_g = __builtin_amdgcn_readlane(t.ew, src);
+    const int32_t i_g = __builtin_amdgcn_readlane(ci, src);
+    const int32_t j_g = __builtin_amdgcn_readlane(cj, src);
+    if (grp == g) {
+      fits = fg;
+      a_star = ag;
+      win_eh = eh_g;
+      win_ew = ew_g;
+      win_i = i_g;
+      win_j = j_g;
+    }
+  }
 
   SampleParams p{};
   p.flip = has_flip ? (word_to_unit(w0) < a.flip_p ? 1 : 0) : 0;
@@ -323,7 +342,6 @@ __device__ __forceinline__ SampleParams draw_sample_params16(const DrawArgs& a, 
   p.words_used = has_flip + has_gate;
   const bool tried = has_gate && word_to_unit(w_gate) < a.erase_p;
   if (tried && fits) {
-    const int a_star = win - leader;
     p.erase = 1;
     p.attempt = a_star;
     p.eh = win_eh;

@@ -1,20 +1,24 @@
 // fn_kernels.hpp -- the GPU kernels of libfn.so (gfx950, wave64).
 //
 //   params_kernel          four samples per wavefront: each sample's decisions.
-//   fused_grouped_kernel   the one-pass operation (page "(11)
-//                          FusedNormalization", section 5) for images whose
-//                          width is a multiple of the pixel group PX: each
-//                          lane owns groups of PX consecutive pixels of one
-//                          row.  A flipped group reads the mirrored group of
-//                          the same row (also PX contiguous pixels) and
-//                          reverses the pixel order in registers, keeping
-//                          the channel order; a group wholly inside the erase
-//                          rectangle reads nothing; values are one fma each
-//                          and are stored as fp32 or round-to-nearest-even
-//                          fp16 in 16-byte vectors.
+//   fused_tiles_kernel     the one-pass operation (page "(11)
+//                          FusedNormalization", section 5), used whenever a
+//                          row holds whole 16-byte output vectors and the
+//                          output is 16-byte aligned: one tile of whole rows
+//                          (or whole images) per work-group, staged in LDS by
+//                          global-to-LDS DMA while the tile's decisions are
+//                          drawn; each lane then writes 16-byte vectors of a
+//                          row, reading flipped sources from LDS.
+//   fused_grouped_kernel   the same operation when the tiles kernel does not
+//                          apply but the width is a multiple of a pixel group
+//                          PX: each lane owns groups of PX consecutive pixels
+//                          of one row; a flipped group reads the mirrored
+//                          group of the same row and reverses the pixel order
+//                          in registers, keeping the channel order; a group
+//                          wholly inside the erase rectangle reads nothing.
 //   fused_generic_kernel   the same operation for any shape and alignment,
-//                          one element at a time (used when the grouped
-//                          kernel's shape or alignment conditions fail).
+//                          one element at a time.
+//   Values are one fma each, stored as fp32 or round-to-nearest-even fp16.
 //   erase_dims_kernel,
 //   cr_ops_kernel,
 //   copy_kernel            test and measurement hooks.
@@ -27,7 +31,7 @@
 
 namespace fn {
 
-// Build-time tuning of the grouped kernel (defaults chosen by measurement):
+// Build-time tuning of the grouped kernel:
 //   FN_GROUP_PX_MAX  widest pixel group tried (16, 8 or 4)
 //   FN_GROUP_ITER    pixel groups per lane (1..4)
 //   FN_NT_STORE      output stores: 0 default, 1 non-temporal, 2 streaming
@@ -42,19 +46,20 @@ namespace fn {
 #define FN_NT_STORE 1
 #endif
 
+// Tiles kernel (defaults chosen by measurement):
+//   FN_TILE_BYTES      most input bytes of one tile
+//   FN_MIN_TILE_BYTES  smallest tile the plan shrinks to for small batches
 #ifndef FN_TILE_BYTES
-#define FN_TILE_BYTES 16384
+#define FN_TILE_BYTES 8192
 #endif
-#ifndef FN_WG_PER_CU
-#define FN_WG_PER_CU 3  // 0: no cap, one tile per work-group
+#ifndef FN_MIN_TILE_BYTES
+#define FN_MIN_TILE_BYTES 2048
 #endif
 
 constexpr int kBlock = 256;             // four wave64 wavefronts
-constexpr int kTileBytesTarget = FN_TILE_BYTES;  // input bytes of one tile
-constexpr int kWgPerCu = FN_WG_PER_CU;           // rows-kernel work-groups per compute unit
-constexpr int kMinTilesPerCu = 2;                // smaller tiles when a batch gives fewer
-constexpr int kTileBytesMax = 16384;    // largest tile the rows kernel stages in LDS
-constexpr int kRowsBlock = 512;         // rows kernel: one producer + seven consumer wavefronts
+constexpr int kTileBytesTarget = FN_TILE_BYTES;
+constexpr int kMinTileBytes = FN_MIN_TILE_BYTES;
+constexpr int kTileBytesMax = 24576;    // largest tile (one row at least) staged in LDS
 constexpr int kMaxImagesPerBlock = 16;  // images whose decisions one work-group draws
 constexpr int kMaxIter = FN_GROUP_ITER;  // pixel groups per lane in the grouped kernel
 constexpr int kGroupPxMax = FN_GROUP_PX_MAX;
@@ -86,11 +91,11 @@ struct FusedArgs {
   uint32_t groups_per_row;    // W / PX
   FastDiv div_gpi, div_gpr;
   int32_t iter;               // groups per lane, 1..kMaxIter
-  // rows kernel: a tile is rows_per_tile rows of one image, or
+  // tiles kernel: a tile is rows_per_tile rows of one image, or
   // images_per_tile whole images
   int32_t images_per_tile;
   int64_t total_tiles;
-  int32_t lds_buffer_bytes;   // one of the two LDS staging buffers
+  int32_t lds_buffer_bytes;   // the LDS staging buffer of one tile
   int64_t total_bytes;        // N * H * W * C
   FastDiv div_row;            // by W * C
   FastDiv div_h;              // by H
@@ -296,7 +301,7 @@ __global__ void __launch_bounds__(kBlock) fused_grouped_kernel(FusedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiles of the rows kernel: a tile is a run of whole rows -- rows_per_tile
+// Tiles of the tiles kernel: a tile is a run of whole rows -- rows_per_tile
 // rows of one image (images_per_tile == 1), or images_per_tile whole images.
 struct Tile {
   int64_t n_first;  // first image
@@ -334,89 +339,6 @@ __device__ __forceinline__ void tile_row_image(const FusedArgs& a, const Tile& T
     *slot = (uint32_t)(T.n_first - n_base) + img;
     *h = r - (int32_t)img * a.H;
   }
-}
-
-// Producer side: moves tile T's input bytes into the LDS buffer `buf` (byte
-// b of the tile at buf[head + b], head = the tile start's offset within its
-// 16-byte granule).  One wavefront issues the granules 64 at a time as
-// global-to-LDS DMA loads (lane l of a batch lands at 16*l past the batch's
-// base).  With `skip`, a granule whose tile bytes all lie in an erased
-// source region is not read.  Granules that straddle the ends of the input
-// buffer are read byte by byte, so nothing outside it is read.  The caller
-// waits for the loads (vmcnt) before releasing the buffer to consumers.
-template <int C>
-__device__ __forceinline__ int32_t issue_tile(const FusedArgs& a, const Tile& T, int64_t n_base,
-                                              const SampleParams* s_params, bool skip,
-                                              uint8_t* buf) {
-  const int32_t row = a.W * C;
-  const int lane = (int)(threadIdx.x & 63u);
-  const uintptr_t in_lo = (uintptr_t)a.in, in_hi = in_lo + (uintptr_t)a.total_bytes;
-  const uintptr_t t_lo = in_lo + (uintptr_t)T.start;
-  const uintptr_t gbase = t_lo & ~(uintptr_t)15;
-  const int32_t head = (int32_t)(t_lo - gbase);
-  const int32_t ngran = (head + T.len + 15) >> 4;
-  // Single-image tile: the erased source block is rows [er0, er1) of the
-  // tile, bytes [se0, se1) of each of those rows (empty when not erasing).
-  int32_t er0 = 0, er1 = 0, se0 = 0, se1 = 0;
-  const bool single = a.images_per_tile == 1;
-  if (skip && single) {
-    const SampleParams& P = s_params[T.n_first - n_base];
-    if (P.erase) {
-      er0 = max(P.i - T.h0, 0);
-      er1 = min(P.i + P.eh - T.h0, T.rows);
-      se0 = (P.flip ? a.W - P.j - P.ew : P.j) * C;
-      se1 = se0 + P.ew * C;
-    }
-  }
-  const bool any_erased = er0 < er1 || (skip && !single);
-  for (int32_t batch = 0; batch < ngran; batch += 64) {
-    const int32_t g = batch + lane;
-    bool load = g < ngran;
-    if (load && any_erased) {
-      // tile bytes held by this granule: [b_lo, b_hi] (tile-relative, inclusive)
-      const int32_t b_lo = max(16 * g - head, 0);
-      const int32_t b_hi = min(16 * g + 15 - head, T.len - 1);
-      const uint32_t r_lo = fast_div((uint32_t)b_lo, a.div_row);
-      const uint32_t r_hi = fast_div((uint32_t)b_hi, a.div_row);
-      if (r_lo == r_hi) {
-        const int32_t x_lo = b_lo - (int32_t)r_lo * row;
-        const int32_t x_hi = b_hi - (int32_t)r_lo * row;
-        if (single) {
-          if ((int32_t)r_lo >= er0 && (int32_t)r_lo < er1 && x_lo >= se0 && x_hi < se1) load = false;
-        } else {
-          uint32_t slot;
-          int32_t h;
-          tile_row_image(a, T, n_base, (int32_t)r_lo, &slot, &h);
-          const SampleParams& P = s_params[slot];
-          if (P.erase && h >= P.i && h < P.i + P.eh) {
-            const int32_t s0 = (P.flip ? a.W - P.j - P.ew : P.j) * C;
-            if (x_lo >= s0 && x_hi < s0 + P.ew * C) load = false;
-          }
-        }
-      }
-    }
-    const uintptr_t A = gbase + 16 * (uintptr_t)g;
-    if (load && A >= in_lo && A + 16 <= in_hi) {
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(A),
-                                       (__attribute__((address_space(3))) void*)(buf + 16 * batch),
-                                       16, 0, 0);
-    } else if (load) {  // the buffer's first or last granule, not fully inside it
-      for (int b = 0; b < 16; ++b) {
-        const uintptr_t addr = A + (uintptr_t)b;
-        if (addr >= in_lo && addr < in_hi) buf[16 * g + b] = *reinterpret_cast<const uint8_t*>(addr);
-      }
-    }
-  }
-  return head;
-}
-
-// Work-group barrier that orders LDS only: the caller has already waited for
-// whatever must be complete (the producer's DMA loads); outstanding global
-// stores of the consumers are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------------------
@@ -485,109 +407,109 @@ struct ChunkSetup {
 };
 
 // ---------------------------------------------------------------------------
-// fused_rows_kernel: work-group b owns tiles [b*T/G, (b+1)*T/G) of the T
-// tiles (G work-groups), consecutive runs of whole rows.  Wavefront 0 is the
-// producer, the other seven are consumers; the two roles never share a
-// memory counter, so the producer waits only for its loads and the
-// consumers never wait for their stores.
-//   producer: DMA the first tile into LDS buffer 0 (no skipping: the
-//     decisions are being drawn meanwhile); then, while the consumers work
-//     on tile i, DMA tile i+1 into the other buffer, skipping wholly erased
-//     granules.
-//   consumers: draw the decisions of every image the range touches (16
-//     lanes per image, in parallel); then per tile, each lane makes
-//     E = 16/sizeof(OutT) consecutive output elements of a row and stores
-//     them as one 16-byte vector, lane-contiguous across the wavefront.
-//     Output element x of a row (x = w*C + c) takes source byte
-//     (W-1-w)*C + c of the same row when the image is flipped, byte x when
-//     not; inside the erase rectangle it is +0.
-//   One LDS barrier per tile hands a filled buffer to the consumers and the
-//   drained one back to the producer.
-// Requires W*C a multiple of E (chunks never cross rows) and a 16-byte
+// Wavefronts first .. first + count - 1 of the work-group move tile T's input
+// bytes into `buf` (byte b of the tile at buf[head + b], head = the tile
+// start's offset within its 16-byte granule): batch k of 64 granules goes to
+// wavefront first + (k mod count) as one global-to-LDS DMA load.  Granules
+// that straddle the ends of the input buffer are read byte by byte.  `index`
+// = this wavefront's number minus `first`; both are wavefront-uniform.
+__device__ __forceinline__ void load_tile_waves(const FusedArgs& a, const Tile& T, uint8_t* buf,
+                                                int32_t index, int32_t count) {
+  const int lane = (int)(threadIdx.x & 63u);
+  const uintptr_t in_lo = (uintptr_t)a.in, in_hi = in_lo + (uintptr_t)a.total_bytes;
+  const uintptr_t t_lo = in_lo + (uintptr_t)T.start;
+  const uintptr_t gbase = t_lo & ~(uintptr_t)15;
+  const int32_t head = (int32_t)(t_lo - gbase);
+  const int32_t ngran = (head + T.len + 15) >> 4;
+  const bool interior = gbase >= in_lo && gbase + 16 * (uintptr_t)ngran <= in_hi;
+  for (int32_t batch = 64 * index; batch < ngran; batch += 64 * count) {
+    const int32_t g = batch + lane;
+    const uintptr_t A = gbase + 16 * (uintptr_t)g;
+    if (g < ngran && (interior || (A >= in_lo && A + 16 <= in_hi))) {
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(A),
+                                       (__attribute__((address_space(3))) void*)(buf + 16 * batch),
+                                       16, 0, 0);
+    } else if (g < ngran) {
+      for (int b = 0; b < 16; ++b) {
+        const uintptr_t addr = A + (uintptr_t)b;
+        if (addr >= in_lo && addr < in_hi) buf[16 * g + b] = *reinterpret_cast<const uint8_t*>(addr);
+      }
+    }
+  }
+}
+
+// Work-group size of the tiles kernel: 256 lanes for 8-element (fp16) chunks,
+// 512 for 4-element (fp32) chunks, so that a pass covers whole rows of
+// typical widths with few idle lanes.
+template <typename OutT>
+constexpr int tiles_threads() {
+  return sizeof(OutT) == 2 ? 256 : 512;
+}
+
+// The fused pass, one tile per work-group (grid = total_tiles).  The first
+// ceil(images / 4) wavefronts draw the decisions of the tile's images (a
+// 16-lane group per image) while the other wavefronts DMA the tile into LDS
+// (when every wavefront draws, all of them load afterwards).  After one
+// barrier every lane makes E = 16/sizeof(OutT) consecutive output elements
+// of a row at a time and stores them as one 16-byte vector, lane-contiguous
+// across the wavefront.  Many small independent work-groups per compute unit
+// hide the memory latency.  Requires W*C a multiple of E and a 16-byte
 // aligned output.
 template <int C, typename OutT>
-__global__ void __launch_bounds__(kRowsBlock) fused_rows_kernel(FusedArgs a) {
+__global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(FusedArgs a) {
+  constexpr int kThreads = tiles_threads<OutT>();
+  constexpr int kWaves = kThreads / 64;
   constexpr int E = 16 / (int)sizeof(OutT);
   extern __shared__ __align__(16) uint8_t s_lds[];
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
-  const int64_t t_begin = (int64_t)blockIdx.x * a.total_tiles / gridDim.x;
-  const int64_t t_end = ((int64_t)blockIdx.x + 1) * a.total_tiles / gridDim.x;
-  if (t_begin >= t_end) return;  // whole work-group
-  const int32_t ntiles = (int32_t)(t_end - t_begin);
-  const Tile first = tile_at(a, t_begin);
-  const Tile last = tile_at(a, t_end - 1);
-  const int64_t n_base = first.n_first;
-  const int n_count = (int)(last.n_first + (last.rows - 1) / a.H - n_base + 1);
-  uint8_t* const buf0 = s_lds;
-  uint8_t* const buf1 = s_lds + a.lds_buffer_bytes;
-
-  if (threadIdx.x < 64) {
-    // ---------------- producer ----------------
-    issue_tile<C>(a, first, n_base, s_params, false, buf0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads have landed
-    lds_barrier();                  // decisions drawn, tile 0 staged
-    for (int32_t i = 0; i + 1 < ntiles; ++i) {
-      issue_tile<C>(a, tile_at(a, t_begin + i + 1), n_base, s_params, true, (i & 1) ? buf0 : buf1);
-      __builtin_amdgcn_s_waitcnt(0);
-      lds_barrier();
-    }
-    return;
+  const Tile T = tile_at(a, blockIdx.x);
+  const int n_count = (T.rows - 1) / a.H + 1;
+  const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+  const int32_t draw_waves = min(kWaves, (n_count + 3) >> 2);
+  const int32_t load_first = draw_waves < kWaves ? draw_waves : 0;
+  if (wave < draw_waves) {
+    const int slot = (int)(threadIdx.x >> 4);
+    const SampleParams p = draw_sample_params16(a.draw, (uint64_t)(T.n_first + slot));
+    if ((threadIdx.x & 15u) == 0 && slot < n_count) s_params[slot] = p;
   }
+  if (wave >= load_first) load_tile_waves(a, T, s_lds, wave - load_first, kWaves - load_first);
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's DMA loads have landed
+  __syncthreads();
 
-  // ---------------- consumers ----------------
-  const int ct = (int)threadIdx.x - 64;  // consumer thread, 0 .. kRowsBlock - 65
-  {
-    const int wave = ct >> 6;
-    if (wave * 4 < n_count) {
-      const int slot = ct >> 4;
-      const SampleParams p = draw_sample_params16(a.draw, (uint64_t)(n_base + slot));
-      if ((ct & 15) == 0 && slot < n_count) s_params[slot] = p;
-    }
-  }
-  lds_barrier();
-
+  const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
   const int32_t row = a.W * C;
   const int32_t cpr = row / E;  // chunks per row
-  constexpr int kConsumers = kRowsBlock - 64;
-  const int32_t rpi = cpr <= kConsumers ? kConsumers / cpr : 0;  // rows per pass when a row fits
-  const int32_t slot_row = rpi ? ct / cpr : 0;
-  const bool active = rpi ? slot_row < rpi : true;
-  const ChunkSetup<C, E> cs(a, rpi ? (ct - slot_row * cpr) * E : 0);
-
-  for (int32_t i = 0; i < ntiles; ++i) {
-    const Tile T = tile_at(a, t_begin + i);
-    const uint8_t* buf = (i & 1) ? buf1 : buf0;
-    const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
-    OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + T.start;
-    if (rpi) {
-      if (active) {
-        for (int32_t r = slot_row; r < T.rows; r += rpi) {
-          uint32_t slot;
-          int32_t h;
-          tile_row_image(a, T, n_base, r, &slot, &h);
-          float v[E];
-          cs.values(buf, head + r * row, s_params[slot], h, v);
-          store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
-        }
-      }
-    } else {
-      // rows wider than one pass of the consumers: per-chunk setup
-      const int32_t nchunks = T.len / E;
-      for (int32_t q = ct; q < nchunks; q += kConsumers) {
-        const int32_t off = q * E;
-        const uint32_t r = fast_div((uint32_t)off, a.div_row);
-        const int32_t x0 = off - (int32_t)r * row;
+  const int ct = (int)threadIdx.x;
+  OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + T.start;
+  if (cpr <= kThreads) {
+    const int32_t rpi = kThreads / cpr;  // rows per pass
+    const int32_t slot_row = ct / cpr;
+    if (slot_row < rpi) {
+      const ChunkSetup<C, E> cs(a, (ct - slot_row * cpr) * E);
+      for (int32_t r = slot_row; r < T.rows; r += rpi) {
         uint32_t slot;
         int32_t h;
-        tile_row_image(a, T, n_base, (int32_t)r, &slot, &h);
-        const ChunkSetup<C, E> cq(a, x0);
+        tile_row_image(a, T, T.n_first, r, &slot, &h);
         float v[E];
-        cq.values(buf, head + (int32_t)r * row, s_params[slot], h, v);
-        store_group<OutT, E>(out + off, v);
+        cs.values(s_lds, head + r * row, s_params[slot], h, v);
+        store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
       }
     }
-    if (i + 1 < ntiles) lds_barrier();  // done with this buffer; the next one is staged
+  } else {
+    const int32_t nchunks = T.len / E;
+    for (int32_t q = ct; q < nchunks; q += kThreads) {
+      const int32_t off = q * E;
+      const uint32_t r = fast_div((uint32_t)off, a.div_row);
+      const int32_t x0 = off - (int32_t)r * row;
+      uint32_t slot;
+      int32_t h;
+      tile_row_image(a, T, T.n_first, (int32_t)r, &slot, &h);
+      const ChunkSetup<C, E> cq(a, x0);
+      float v[E];
+      cq.values(s_lds, head + (int32_t)r * row, s_params[slot], h, v);
+      store_group<OutT, E>(out + off, v);
+    }
   }
 }
 

@@ -20,6 +20,10 @@ Prints ONE JSON line:
   cpu_baseline  the oracle (plain C loops, fp32 output) timed on this
              host's cores over a bounded sample of the same workload.
 
+Timing: about --prewarm-seconds of untimed launches (the GPU clocks down
+while the host builds inputs), --warmup untimed launches, then --steps timed
+launches between two device synchronisations.
+
 Extra legs: a plain 16-byte copy kernel moving the same byte count gives
 the practical bandwidth ceiling; --all adds one line per workload on
 stderr.
@@ -38,7 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fused_rows_kernel_imagenet_train_counters.txt")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fused_tiles_kernel_imagenet_train_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "augmentation_amd", "csrc", f)
                   for f in ("fn_api.hip", "fn_kernels.hpp", "fn_device.hpp", "exp2_table.inc")]
 
@@ -91,10 +95,18 @@ def host_threads() -> int:
     return max(1, min(n, 16))  # the machine's CPU share for one GPU
 
 
-def time_launches(launch, steps: int, warmup: int, sets: int, stream) -> float:
+def time_launches(launch, steps: int, warmup: int, sets: int, stream, prewarm_s: float) -> float:
     """Average milliseconds per launch over `steps` launches (events on the
-    launch stream), after `warmup` untimed ones."""
+    launch stream), after `warmup` untimed ones.  Before those, launches run
+    untimed for about `prewarm_s` seconds: the GPU clocks down while the host
+    prepares inputs, and a few warmup launches (well under a millisecond)
+    do not bring it back up."""
     import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < prewarm_s:
+        for k in range(50):
+            launch(k % sets)
+        torch.cuda.synchronize()
     for k in range(warmup):
         launch(k % sets)
     torch.cuda.synchronize()
@@ -108,7 +120,7 @@ def time_launches(launch, steps: int, warmup: int, sets: int, stream) -> float:
     return start.elapsed_time(end) / steps
 
 
-def bench_workload(b, w, steps: int, warmup: int, sets: int, seed_base: int = 123) -> dict:
+def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -> dict:
     import torch
     stream = torch.cuda.current_stream()
     x = torch.from_numpy(w.make_input()).cuda()
@@ -123,14 +135,14 @@ def bench_workload(b, w, steps: int, warmup: int, sets: int, seed_base: int = 12
                              w.scale[0], w.scale[1], w.ratio[0], w.ratio[1],
                              seeds[k % len(seeds)], w.out_dtype, outs[k], stream)
 
-    ms = time_launches(launch, steps, warmup, sets, stream)
+    ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s)
     del ins, outs
     torch.cuda.empty_cache()
     return {"ms": ms, "images_per_s": w.N / (ms * 1e-3),
             "gbs": w.nominal_bytes / (ms * 1e-3) / 1e9}
 
 
-def bench_copy(b, nbytes: int, steps: int, warmup: int, sets: int) -> dict:
+def bench_copy(b, nbytes: int, steps: int, warmup: int, sets: int, prewarm_s: float) -> dict:
     """The plain copy kernel moving nbytes per launch (nbytes/2 read, nbytes/2 written)."""
     import torch
     stream = torch.cuda.current_stream()
@@ -143,7 +155,7 @@ def bench_copy(b, nbytes: int, steps: int, warmup: int, sets: int) -> dict:
     def launch(k):
         b.fn_test_copy(src[k], dst[k], half, stream)
 
-    ms = time_launches(launch, steps, warmup, sets, stream)
+    ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s)
     del src, dst
     torch.cuda.empty_cache()
     return {"ms": ms, "gbs": 2 * half / (ms * 1e-3) / 1e9, "bytes": 2 * half}
@@ -176,6 +188,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=10, help="rotating buffer sets")
+    ap.add_argument("--prewarm-seconds", type=float, default=0.3,
+                    help="untimed launches before the warmup ones")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true")
@@ -196,7 +210,7 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[synth.HEADLINE]
-    r = bench_workload(b, w, args.steps, args.warmup, args.sets)
+    r = bench_workload(b, w, args.steps, args.warmup, args.sets, args.prewarm_seconds)
     achieved = r["gbs"]
     traffic = counter_traffic()
 
@@ -223,13 +237,14 @@ def main() -> int:
                      "bytes_per_launch": w.nominal_bytes},
     }
     if not args.no_copy:
-        c = bench_copy(b, w.nominal_bytes, args.steps, args.warmup, args.sets)
+        c = bench_copy(b, w.nominal_bytes, args.steps, args.warmup, args.sets, args.prewarm_seconds)
         line["copy_ceiling"] = {"gbs": round(c["gbs"], 1), "bytes_per_launch": c["bytes"],
                                 "ms": round(c["ms"], 5),
                                 "fused_vs_copy": round(achieved / c["gbs"], 4)}
     if args.all:
         for name, wl in synth.WORKLOADS.items():
-            rr = bench_workload(b, wl, max(10, args.steps // 4), 5, args.sets if wl.N < 1024 else 2)
+            rr = bench_workload(b, wl, max(10, args.steps // 4), 5, args.sets if wl.N < 1024 else 2,
+                                args.prewarm_seconds)
             print(json.dumps({"workload": name, "ms_per_launch": round(rr["ms"], 5),
                               "images_per_s": round(rr["images_per_s"], 1),
                               "gbs_nominal": round(rr["gbs"], 1),
