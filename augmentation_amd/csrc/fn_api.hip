@@ -133,6 +133,45 @@ int device_cu_count(int* cus) {
   return FN_OK;
 }
 
+// LDS bytes per compute unit of the current device, cached per device; 0 if
+// the runtime does not report it.
+size_t device_lds_per_cu() {
+  static std::atomic<long> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev >= 0 && dev < 64) {
+    const long c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c > 0 ? (size_t)c : 0;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    v = 0;
+  }
+  if (dev >= 0 && dev < 64) cache[dev].store(v > 0 ? (long)v : -1, std::memory_order_relaxed);
+  return v > 0 ? (size_t)v : 0;
+}
+
+// Dynamic LDS of one tiles-kernel work-group: its staging buffer, padded so
+// that at most kWgsPerCu work-groups fit on a compute unit (fewer resident
+// work-groups queue less at the memory and finish sooner; measured).  The
+// padding never exceeds the 64 KB a work-group may request.
+size_t tiles_lds_bytes(int32_t buffer_bytes) {
+  size_t lds = (size_t)buffer_bytes;
+  const size_t per_cu = device_lds_per_cu();
+  if (fn::kWgsPerCu > 0 && per_cu > 0) {
+    const size_t cap = per_cu / fn::kWgsPerCu;   // kWgsPerCu fit ...
+    const size_t over = per_cu / (fn::kWgsPerCu + 1) + 1;  // ... one more does not
+    const size_t want = cap - 1024;  // room for the static decision records
+    if (want >= over && want <= 65536) lds = std::max(lds, want);
+  }
+  return lds;
+}
+
 fn::FastDiv make_fast_div(uint32_t d) {
   fn::FastDiv f;
   f.d = d;
@@ -267,7 +306,7 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
                                  float erase_p, float scale_min, float scale_max, float ratio_min,
                                  float ratio_max, uint64_t seed, int32_t out_dtype, void* out_dev,
                                  void* stream) {
-  fn::FusedArgs a;
+  fn::FusedArgs a{};
   int rc = make_draw_args(seed, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
                           &a.draw);
   if (rc) return rc;
@@ -333,7 +372,8 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
     if (rc) return rc;
     a.div_row = make_fast_div((uint32_t)row);
     a.div_h = make_fast_div((uint32_t)H);
-    launch_tiles(a, C, out_dtype, (unsigned)a.total_tiles, (size_t)a.lds_buffer_bytes, st);
+    a.div_tpi = make_fast_div((uint32_t)a.tiles_per_image);
+    launch_tiles(a, C, out_dtype, (unsigned)a.total_tiles, tiles_lds_bytes(a.lds_buffer_bytes), st);
     return launch_status("fused_tiles_kernel launch");
   }
   const int px = pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);

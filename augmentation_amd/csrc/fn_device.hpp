@@ -38,8 +38,10 @@ __device__ __forceinline__ Block4 philox4x32_10(uint32_t c0, uint32_t c1, uint32
   constexpr uint32_t kWeyl0 = 0x9E3779B9u, kWeyl1 = 0xBB67AE85u;
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t hi_a = __umulhi(kMulA, c0), lo_a = kMulA * c0;
-    const uint32_t hi_b = __umulhi(kMulB, c2), lo_b = kMulB * c2;
+    // one 32x32->64 multiply (v_mad_u64_u32) gives both halves
+    const uint64_t pa = (uint64_t)kMulA * c0, pb = (uint64_t)kMulB * c2;
+    const uint32_t hi_a = (uint32_t)(pa >> 32), lo_a = (uint32_t)pa;
+    const uint32_t hi_b = (uint32_t)(pb >> 32), lo_b = (uint32_t)pb;
     const uint32_t n0 = hi_b ^ c1 ^ k0, n2 = hi_a ^ c3 ^ k1;
     c0 = n0;
     c1 = lo_b;

@@ -49,16 +49,22 @@ namespace fn {
 // Tiles kernel (defaults chosen by measurement):
 //   FN_TILE_BYTES      most input bytes of one tile
 //   FN_MIN_TILE_BYTES  smallest tile the plan shrinks to for small batches
+//   FN_WGS_PER_CU      most work-groups resident on a compute unit (0: no
+//                      cap); enforced through the LDS size each requests
 #ifndef FN_TILE_BYTES
 #define FN_TILE_BYTES 8192
 #endif
 #ifndef FN_MIN_TILE_BYTES
 #define FN_MIN_TILE_BYTES 2048
 #endif
+#ifndef FN_WGS_PER_CU
+#define FN_WGS_PER_CU 6
+#endif
 
 constexpr int kBlock = 256;             // four wave64 wavefronts
 constexpr int kTileBytesTarget = FN_TILE_BYTES;
 constexpr int kMinTileBytes = FN_MIN_TILE_BYTES;
+constexpr int kWgsPerCu = FN_WGS_PER_CU;
 constexpr int kTileBytesMax = 24576;    // largest tile (one row at least) staged in LDS
 constexpr int kMaxImagesPerBlock = 16;  // images whose decisions one work-group draws
 constexpr int kMaxIter = FN_GROUP_ITER;  // pixel groups per lane in the grouped kernel
@@ -99,6 +105,7 @@ struct FusedArgs {
   int64_t total_bytes;        // N * H * W * C
   FastDiv div_row;            // by W * C
   FastDiv div_h;              // by H
+  FastDiv div_tpi;            // by tiles_per_image
   float mul[4];               // RN32(1 / (255 std_c))
   float nsub[4];              // -RN32(mean_c / std_c)
   DrawArgs draw;
@@ -311,15 +318,16 @@ struct Tile {
   int32_t len;      // input bytes = output elements
 };
 
-__device__ __forceinline__ Tile tile_at(const FusedArgs& a, int64_t t) {
+__device__ __forceinline__ Tile tile_at(const FusedArgs& a, uint32_t t) {
   Tile T;
   const int32_t row = a.W * a.C;
   if (a.images_per_tile == 1) {
-    T.n_first = t / a.tiles_per_image;
-    T.h0 = (int32_t)(t - T.n_first * a.tiles_per_image) * a.rows_per_tile;
+    const uint32_t n = fast_div(t, a.div_tpi);
+    T.n_first = n;
+    T.h0 = (int32_t)(t - n * (uint32_t)a.tiles_per_image) * a.rows_per_tile;
     T.rows = min(a.rows_per_tile, a.H - T.h0);
   } else {
-    T.n_first = t * a.images_per_tile;
+    T.n_first = (int64_t)t * a.images_per_tile;
     T.h0 = 0;
     T.rows = (int32_t)min((int64_t)a.images_per_tile, a.N - T.n_first) * a.H;
   }
@@ -482,18 +490,31 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   const int32_t cpr = row / E;  // chunks per row
   const int ct = (int)threadIdx.x;
   OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + T.start;
+  // A tile of one image reads its decision record into registers once;
+  // tiles of several images look up each row's record.
+  const bool single = a.images_per_tile == 1;
+  const SampleParams P0 = s_params[0];
   if (cpr <= kThreads) {
     const int32_t rpi = kThreads / cpr;  // rows per pass
     const int32_t slot_row = ct / cpr;
     if (slot_row < rpi) {
       const ChunkSetup<C, E> cs(a, (ct - slot_row * cpr) * E);
-      for (int32_t r = slot_row; r < T.rows; r += rpi) {
-        uint32_t slot;
-        int32_t h;
-        tile_row_image(a, T, T.n_first, r, &slot, &h);
-        float v[E];
-        cs.values(s_lds, head + r * row, s_params[slot], h, v);
-        store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
+      if (single) {
+        for (int32_t r = slot_row; r < T.rows; r += rpi) {
+          float v[E];
+          cs.values(s_lds, head + r * row, P0, T.h0 + r, v);
+          store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
+        }
+      } else {
+        for (int32_t r = slot_row; r < T.rows; r += rpi) {
+          uint32_t slot;
+          int32_t h;
+          tile_row_image(a, T, T.n_first, r, &slot, &h);
+          const SampleParams P = s_params[slot];
+          float v[E];
+          cs.values(s_lds, head + r * row, P, h, v);
+          store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
+        }
       }
     }
   } else {
@@ -505,9 +526,10 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       uint32_t slot;
       int32_t h;
       tile_row_image(a, T, T.n_first, (int32_t)r, &slot, &h);
+      const SampleParams P = single ? P0 : s_params[slot];
       const ChunkSetup<C, E> cq(a, x0);
       float v[E];
-      cq.values(s_lds, head + (int32_t)r * row, s_params[slot], h, v);
+      cq.values(s_lds, head + (int32_t)r * row, P, h, v);
       store_group<OutT, E>(out + off, v);
     }
   }
