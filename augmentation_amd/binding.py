@@ -25,7 +25,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 FN_OK, FN_EINVAL, FN_EOVERFLOW, FN_EHIP = 0, -1, -2, -3
-FN_OUT_FP32, FN_OUT_FP16 = 0, 1
+FN_OUT_FP32, FN_OUT_FP16, FN_OUT_FP16_PAD4 = 0, 1, 2
 
 # fn_sample_params: eight int32 fields, 32 bytes
 PARAMS_DTYPE = np.dtype(
@@ -132,15 +132,17 @@ def fused_normalize(x: torch.Tensor, mean, std, flip_p=0.5, erase_p=0.0, scale=(
                     ratio=(0.3, 3.3), seed=0, out_dtype=FN_OUT_FP32, out=None,
                     stream=None) -> torch.Tensor:
     """fn_fused_normalize on an (N, H, W, C) uint8 CUDA tensor; returns (or
-    fills) the (N, H, W, C) float32/float16 output tensor."""
+    fills) the (N, H, W, C) float32/float16 output tensor, (N, H, W, 4)
+    float16 for FN_OUT_FP16_PAD4."""
     if x.dtype != torch.uint8 or x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous (N, H, W, C) uint8 CUDA tensor")
     N, H, W, C = x.shape
     tdt = torch.float32 if out_dtype == FN_OUT_FP32 else torch.float16
+    shape = (N, H, W, 4 if out_dtype == FN_OUT_FP16_PAD4 else C)
     if out is None:
-        out = torch.empty((N, H, W, C), dtype=tdt, device=x.device)
-    elif out.dtype != tdt or tuple(out.shape) != (N, H, W, C) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor of the input's shape and out_dtype")
+        out = torch.empty(shape, dtype=tdt, device=x.device)
+    elif out.dtype != tdt or tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of shape %s and out_dtype" % (shape,))
     fn_fused_normalize(x, N, H, W, C, mean, std, flip_p, erase_p, scale[0], scale[1], ratio[0],
                        ratio[1], seed, out_dtype, out, stream)
     return out

@@ -221,9 +221,11 @@ template <int C>
 void launch_tiles_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t lds,
                     hipStream_t st) {
   if (out_dtype == FN_OUT_FP32)
-    fn::fused_tiles_kernel<C, float><<<grid, fn::tiles_threads<float>(), lds, st>>>(a);
+    fn::fused_tiles_kernel<C, float, false><<<grid, fn::tiles_threads<float>(), lds, st>>>(a);
+  else if (out_dtype == FN_OUT_FP16_PAD4)
+    fn::fused_tiles_kernel<C, _Float16, true><<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
   else
-    fn::fused_tiles_kernel<C, _Float16><<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
+    fn::fused_tiles_kernel<C, _Float16, false><<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
 }
 
 void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
@@ -312,7 +314,7 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
   if (rc) return rc;
   if (C < 1 || C > 4) return fail(FN_EINVAL, "C must be in 1..4 (got %d)", C);
   if (N < 0) return fail(FN_EINVAL, "N must be >= 0");
-  if (out_dtype != FN_OUT_FP32 && out_dtype != FN_OUT_FP16)
+  if (out_dtype != FN_OUT_FP32 && out_dtype != FN_OUT_FP16 && out_dtype != FN_OUT_FP16_PAD4)
     return fail(FN_EINVAL, "unknown out_dtype %d", out_dtype);
   if (mean == nullptr || std == nullptr) return fail(FN_EINVAL, "mean and std must not be NULL");
   for (int c = 0; c < C; ++c) {
@@ -321,9 +323,11 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
       return fail(FN_EINVAL, "std[%d] must be positive and finite", c);
   }
   const int64_t img = (int64_t)H * W * C;
-  if (N > INT64_MAX / 4 / img) return fail(FN_EOVERFLOW, "N*H*W*C*4 overflows int64");
+  if (N > INT64_MAX / 16 / ((int64_t)H * W)) return fail(FN_EOVERFLOW, "N*H*W*4*4 overflows int64");
   const int64_t elems = N * img;
   const int out_bytes = out_dtype == FN_OUT_FP32 ? 4 : 2;
+  const int oc = out_dtype == FN_OUT_FP16_PAD4 ? 4 : C;  // output channels per pixel
+  const int64_t out_elems = N * H * (int64_t)W * oc;
 
   // generic kernel tiles: about 8 KiB of input, whole rows
   const int64_t row = (int64_t)W * C;
@@ -339,10 +343,10 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
     return fail(FN_EINVAL, "out_dev must be aligned to its element size (%d bytes)", out_bytes);
   rc = check_device_range(in_u8_dev, (size_t)elems, "in_u8_dev");
   if (rc) return rc;
-  rc = check_device_range(out_dev, (size_t)elems * out_bytes, "out_dev");
+  rc = check_device_range(out_dev, (size_t)out_elems * out_bytes, "out_dev");
   if (rc) return rc;
   const uintptr_t i0 = (uintptr_t)in_u8_dev, i1 = i0 + (uintptr_t)elems;
-  const uintptr_t o0 = (uintptr_t)out_dev, o1 = o0 + (uintptr_t)elems * out_bytes;
+  const uintptr_t o0 = (uintptr_t)out_dev, o1 = o0 + (uintptr_t)out_elems * out_bytes;
   if (i0 < o1 && o0 < i1) return fail(FN_EINVAL, "input and output overlap");
 
   a.in = in_u8_dev;
@@ -351,6 +355,7 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
   a.H = H;
   a.W = W;
   a.C = C;
+  a.oc = oc;
   for (int c = 0; c < 4; ++c) {
     if (c < C) {
       a.mul[c] = (float)(1.0 / (255.0 * (double)std[c]));
@@ -363,7 +368,8 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
 
   hipStream_t st = (hipStream_t)stream;
   a.total_bytes = elems;
-  if ((uintptr_t)out_dev % 16 == 0 && row % (16 / out_bytes) == 0 &&
+  const int64_t row_out = (int64_t)W * oc;
+  if ((uintptr_t)out_dev % 16 == 0 && row_out % (16 / out_bytes) == 0 &&
       row <= fn::kTileBytesMax) {
     int cus = 0;
     rc = device_cu_count(&cus);
@@ -371,12 +377,15 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
     rc = plan_tiles(&a, N, H, row, elems, cus);
     if (rc) return rc;
     a.div_row = make_fast_div((uint32_t)row);
+    a.div_row_out = make_fast_div((uint32_t)row_out);
     a.div_h = make_fast_div((uint32_t)H);
     a.div_tpi = make_fast_div((uint32_t)a.tiles_per_image);
     launch_tiles(a, C, out_dtype, (unsigned)a.total_tiles, tiles_lds_bytes(a.lds_buffer_bytes), st);
     return launch_status("fused_tiles_kernel launch");
   }
-  const int px = pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);
+  const int px = out_dtype == FN_OUT_FP16_PAD4
+                     ? 0
+                     : pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);
   if (px > 0) {
     a.groups_per_row = (uint32_t)(W / px);
     a.groups_per_image = (uint32_t)((int64_t)H * W / px);

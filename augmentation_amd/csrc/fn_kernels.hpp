@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fn_device.hpp"
 
 namespace fn {
@@ -89,6 +91,7 @@ struct FusedArgs {
   void* out;
   int64_t N;
   int32_t H, W, C;
+  int32_t oc;                 // output channels per pixel: C, or 4 when padded
   // generic kernel: tiles of whole rows
   int32_t rows_per_tile, tiles_per_image;
   // grouped kernel
@@ -104,6 +107,7 @@ struct FusedArgs {
   int32_t lds_buffer_bytes;   // the LDS staging buffer of one tile
   int64_t total_bytes;        // N * H * W * C
   FastDiv div_row;            // by W * C
+  FastDiv div_row_out;        // by W * oc
   FastDiv div_h;              // by H
   FastDiv div_tpi;            // by tiles_per_image
   float mul[4];               // RN32(1 / (255 std_c))
@@ -414,6 +418,52 @@ struct ChunkSetup {
   }
 };
 
+// The padded fp16 layout (page sec. 8): every pixel has 4 output channels,
+// channels c < C normalized, channels C..3 +0.  A lane's 8 outputs are two
+// whole pixels w0, w0 + 1 (x0 = 4 w0); pixel w takes source pixel W-1-w when
+// flipped, channels in order; an erased pixel is +0 in every channel.
+template <int C>
+struct Pad4Chunk {
+  int32_t x0;
+  int32_t w0;
+  int32_t direct, mirror;  // source byte of pixel w0, from the row start, unflipped / flipped
+  float mul[C], nsub[C];
+
+  __device__ __forceinline__ Pad4Chunk(const FusedArgs& a, int32_t first) : x0(first) {
+    w0 = first >> 2;
+    direct = w0 * C;
+    mirror = (a.W - 1 - w0) * C;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      mul[c] = a.mul[c];
+      nsub[c] = a.nsub[c];
+    }
+  }
+
+  __device__ __forceinline__ void values(const uint8_t* s_tile, int32_t row_lds,
+                                         const SampleParams& P, int32_t h, float (&v)[8]) const {
+    const int32_t b0 = row_lds + (P.flip ? mirror : direct);
+    const int32_t step = P.flip ? -C : C;
+    bool er[2] = {false, false};
+    if (P.erase && h >= P.i && h < P.i + P.eh) {
+      er[0] = w0 >= P.j && w0 < P.j + P.ew;
+      er[1] = w0 + 1 >= P.j && w0 + 1 < P.j + P.ew;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c < C) {
+          const float x = (float)s_tile[b0 + p * step + c];
+          v[4 * p + c] = er[p] ? 0.0f : __builtin_fmaf(x, mul[c], nsub[c]);
+        } else {
+          v[4 * p + c] = 0.0f;
+        }
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Wavefronts first .. first + count - 1 of the work-group move tile T's input
 // bytes into `buf` (byte b of the tile at buf[head + b], head = the tile
@@ -463,11 +513,14 @@ constexpr int tiles_threads() {
 // across the wavefront.  Many small independent work-groups per compute unit
 // hide the memory latency.  Requires W*C a multiple of E and a 16-byte
 // aligned output.
-template <int C, typename OutT>
+template <int C, typename OutT, bool kPad4>
 __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(FusedArgs a) {
   constexpr int kThreads = tiles_threads<OutT>();
   constexpr int kWaves = kThreads / 64;
   constexpr int E = 16 / (int)sizeof(OutT);
+  constexpr int OC = kPad4 ? 4 : C;  // output channels per pixel
+  static_assert(!kPad4 || E == 8, "the padded layout is fp16: two pixels per 16-byte vector");
+  using Setup = typename std::conditional<kPad4, Pad4Chunk<C>, ChunkSetup<C, E>>::type;
   extern __shared__ __align__(16) uint8_t s_lds[];
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
@@ -486,10 +539,11 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   __syncthreads();
 
   const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
-  const int32_t row = a.W * C;
-  const int32_t cpr = row / E;  // chunks per row
+  const int32_t row = a.W * C;        // input bytes of a row (as staged in LDS)
+  const int32_t row_out = a.W * OC;   // output elements of a row
+  const int32_t cpr = row_out / E;    // chunks per row
   const int ct = (int)threadIdx.x;
-  OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + T.start;
+  OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + (T.start / C) * OC;
   // A tile of one image reads its decision record into registers once;
   // tiles of several images look up each row's record.
   const bool single = a.images_per_tile == 1;
@@ -498,12 +552,12 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
     const int32_t rpi = kThreads / cpr;  // rows per pass
     const int32_t slot_row = ct / cpr;
     if (slot_row < rpi) {
-      const ChunkSetup<C, E> cs(a, (ct - slot_row * cpr) * E);
+      const Setup cs(a, (ct - slot_row * cpr) * E);
       if (single) {
         for (int32_t r = slot_row; r < T.rows; r += rpi) {
           float v[E];
           cs.values(s_lds, head + r * row, P0, T.h0 + r, v);
-          store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
+          store_group<OutT, E>(out + (int64_t)r * row_out + cs.x0, v);
         }
       } else {
         for (int32_t r = slot_row; r < T.rows; r += rpi) {
@@ -513,21 +567,21 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
           const SampleParams P = s_params[slot];
           float v[E];
           cs.values(s_lds, head + r * row, P, h, v);
-          store_group<OutT, E>(out + (int64_t)r * row + cs.x0, v);
+          store_group<OutT, E>(out + (int64_t)r * row_out + cs.x0, v);
         }
       }
     }
   } else {
-    const int32_t nchunks = T.len / E;
+    const int32_t nchunks = T.rows * cpr;
     for (int32_t q = ct; q < nchunks; q += kThreads) {
       const int32_t off = q * E;
-      const uint32_t r = fast_div((uint32_t)off, a.div_row);
-      const int32_t x0 = off - (int32_t)r * row;
+      const uint32_t r = fast_div((uint32_t)off, a.div_row_out);
+      const int32_t x0 = off - (int32_t)r * row_out;
       uint32_t slot;
       int32_t h;
       tile_row_image(a, T, T.n_first, (int32_t)r, &slot, &h);
       const SampleParams P = single ? P0 : s_params[slot];
-      const ChunkSetup<C, E> cq(a, x0);
+      const Setup cq(a, x0);
       float v[E];
       cq.values(s_lds, head + (int32_t)r * row, P, h, v);
       store_group<OutT, E>(out + off, v);
@@ -544,23 +598,24 @@ __global__ void __launch_bounds__(kBlock) fused_generic_kernel(FusedArgs a) {
   draw_block_params(a.draw, n, 1, s_params);
   const SampleParams p = s_params[0];
 
-  const int32_t W = a.W, C = a.C;
-  const int64_t row_elems = (int64_t)W * C;
+  const int32_t W = a.W, C = a.C, OC = a.oc;
+  const int64_t row_elems = (int64_t)W * C;  // input bytes of a row
+  const int64_t row_out = (int64_t)W * OC;   // output elements of a row
   const int32_t h0 = tile * a.rows_per_tile;
   const int32_t h1 = min(a.H, h0 + a.rows_per_tile);
   const int64_t img_base = n * (int64_t)a.H * row_elems;
-  const int64_t begin = img_base + (int64_t)h0 * row_elems;
-  const int64_t count = (int64_t)(h1 - h0) * row_elems;
+  const int64_t begin = (n * (int64_t)a.H + h0) * row_out;
+  const int64_t count = (int64_t)(h1 - h0) * row_out;
   OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out);
 
   for (int64_t idx = threadIdx.x; idx < count; idx += kBlock) {
-    const int32_t h = h0 + (int32_t)(idx / row_elems);
-    const int32_t rem = (int32_t)(idx % row_elems);
-    const int32_t w = rem / C;
-    const int32_t c = rem - w * C;
+    const int32_t h = h0 + (int32_t)(idx / row_out);
+    const int32_t rem = (int32_t)(idx % row_out);
+    const int32_t w = rem / OC;
+    const int32_t c = rem - w * OC;
     const bool erased = p.erase && h >= p.i && h < p.i + p.eh && w >= p.j && w < p.j + p.ew;
     float v = 0.0f;
-    if (!erased) {
+    if (!erased && c < C) {
       const int32_t src_w = p.flip ? (W - 1 - w) : w;
       const uint8_t x = a.in[img_base + (int64_t)h * row_elems + (int64_t)src_w * C + c];
       v = __builtin_fmaf((float)x, a.mul[c], a.nsub[c]);

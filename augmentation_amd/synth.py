@@ -30,7 +30,7 @@ ERASE_RATIO = (0.3, 3.3)
 # The pages seed their experiments with manual_seed(123).
 PARAM_SEED = 123
 
-OUT_FP32, OUT_FP16 = 0, 1
+OUT_FP32, OUT_FP16, OUT_FP16_PAD4 = 0, 1, 2
 
 
 def uniform_images(rng: np.random.Generator, N: int, H: int, W: int, C: int) -> np.ndarray:
@@ -85,10 +85,18 @@ class Workload:
         return 4 if self.out_dtype == OUT_FP32 else 2
 
     @property
+    def out_channels(self) -> int:
+        return 4 if self.out_dtype == OUT_FP16_PAD4 else self.C
+
+    @property
+    def out_shape(self) -> tuple:
+        return (self.N, self.H, self.W, self.out_channels)
+
+    @property
     def nominal_bytes(self) -> int:
         """Bytes one launch moves by the metric's count: every input byte
         read once and every output element written once, erased or not."""
-        return self.elems * (1 + self.out_bytes)
+        return self.elems + self.N * self.H * self.W * self.out_channels * self.out_bytes
 
     def make_input(self) -> np.ndarray:
         """The whole (N, H, W, C) uint8 batch, from the workload's data seed."""
@@ -107,6 +115,9 @@ WORKLOADS = {
                              0.0, 0.0, OUT_FP32, 1004),
     "stress": Workload("stress", 2048, 224, 224, 3, IMAGENET_MEAN, IMAGENET_STD, 0.5, 1.0,
                        OUT_FP16, 1005, seeds=tuple(range(PARAM_SEED, PARAM_SEED + 8))),
+    # the training batch in the page's 4-channel mixed-precision layout (section 8)
+    "imagenet_train_pad4": Workload("imagenet_train_pad4", 256, 224, 224, 3, IMAGENET_MEAN,
+                                    IMAGENET_STD, 0.5, 0.5, OUT_FP16_PAD4, 1003, kind="gradient"),
 }
 
 # The workload the headline metric is quoted on.

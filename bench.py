@@ -126,7 +126,7 @@ def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -
     x = torch.from_numpy(w.make_input()).cuda()
     tdt = torch.float32 if w.out_dtype == 0 else torch.float16
     ins = [x] + [x.clone() for _ in range(sets - 1)]
-    outs = [torch.empty((w.N, w.H, w.W, w.C), dtype=tdt, device="cuda") for _ in range(sets)]
+    outs = [torch.empty(w.out_shape, dtype=tdt, device="cuda") for _ in range(sets)]
     torch.cuda.synchronize()
     seeds = w.seeds
 

@@ -49,6 +49,9 @@ extern "C" {
 /* Output element type. */
 #define FN_OUT_FP32 0 /* 4-byte IEEE binary32                                       */
 #define FN_OUT_FP16 1 /* 2-byte IEEE binary16, rounded to nearest even (page sec. 6) */
+#define FN_OUT_FP16_PAD4 2 /* binary16 with 4 channels per pixel: channels c < C as
+                              FN_OUT_FP16, channels C..3 are +0 -- the page's
+                              mixed-precision layout (page sec. 8) */
 
 /* One sample's random decisions (32 bytes, all int32):
  *   flip        1 if the image is mirrored left-right, else 0;
@@ -81,9 +84,9 @@ typedef struct {
  *               (page sec. 4 defaults 0.3, 3.3).
  *   seed        64-bit generator key; sample n draws from the stream keyed by
  *               (seed, n), so the result does not depend on the launch shape.
- *   out_dtype   FN_OUT_FP32 or FN_OUT_FP16.
- *   out_dev     N*H*W*C elements of out_dtype, same NHWC layout as the input
- *               (C channels per pixel, no padding), aligned to the element
+ *   out_dtype   FN_OUT_FP32, FN_OUT_FP16 or FN_OUT_FP16_PAD4.
+ *   out_dev     N*H*W*OC elements of out_dtype in NHWC order, OC = C (no
+ *               padding) or 4 for FN_OUT_FP16_PAD4, aligned to the element
  *               size (4 or 2 bytes); must not overlap the input.
  *
  * Result, per sample n with P = fn_params(seed, ...)[n]:
@@ -93,7 +96,8 @@ typedef struct {
  *   x = in[n, h, P.flip ? W-1-w : w, c], mul_c = RN32(1/(255 std_c)),
  *   sub_c = RN32(mean_c/std_c).  The pixel order is mirrored, the channel
  *   order inside a pixel is kept (page sec. 7).  fp16 output is the fp32
- *   value rounded to nearest even.
+ *   value rounded to nearest even.  With FN_OUT_FP16_PAD4, out[n,h,w,c] for
+ *   c < C is the fp16 value above and out[n,h,w,c] = +0 for C <= c < 4.
  *
  * Errors: FN_EINVAL for a null pointer (N > 0), a device pointer that is not
  * device memory or whose buffer is shorter than the sizes above, a misaligned

@@ -72,7 +72,8 @@ def ctypes_floats(v, C):
     (dict(flip_p=1.5), -1), (dict(flip_p=float("nan")), -1), (dict(erase_p=-0.1), -1),
     (dict(scale_min=0.0), -1), (dict(scale_min=0.5, scale_max=0.4), -1), (dict(scale_max=1.5), -1),
     (dict(ratio_min=0.0), -1), (dict(ratio_min=3.0, ratio_max=2.0), -1),
-    (dict(ratio_max=2.0**31), -1), (dict(out_dtype=2), -1), (dict(mean=None), -1),
+    (dict(ratio_max=2.0**31), -1), (dict(out_dtype=3), -1), (dict(out_dtype=-1), -1),
+    (dict(mean=None), -1),
     (dict(std=(0.2, 0.0, 0.2)), -1), (dict(std=(0.2, -1.0, 0.2)), -1),
     (dict(mean=(0.1, float("inf"), 0.1)), -1), (dict(std=(0.2, float("nan"), 0.2)), -1),
     (dict(H=4097, W=4096), -2),
@@ -94,7 +95,8 @@ def test_zero_images_is_a_no_op(b):
 def test_scalar_domain_edges_accepted(b):
     for kw in (dict(flip_p=0.0, erase_p=0.0), dict(flip_p=1.0, erase_p=1.0),
                dict(scale_min=2.0**-30, scale_max=1.0), dict(ratio_min=2.0**-30, ratio_max=2.0**30),
-               dict(H=4096, W=4096, C=1), dict(C=4, mean=(0, 0, 0, 0), std=(1, 1, 1, 1))):
+               dict(H=4096, W=4096, C=1), dict(C=4, mean=(0, 0, 0, 0), std=(1, 1, 1, 1)),
+               dict(out_dtype=2), dict(out_dtype=2, C=1, mean=(0.5,), std=(0.25,))):
         assert call_fused(b, N=0, **kw) == 0, (kw, b.fn_last_error())
 
 
