@@ -38,7 +38,10 @@ _u64, _i64, _i32, _f32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes
 _SIGS = {
     "fn_fused_normalize": [_P, _i64, _i32, _i32, _i32, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                            _u64, _i32, _P, _P],
+    "fn_fused_normalize_ex": [_P, _i64, _i64, _i64, _i32, _i32, _i32, _P, _P, _f32, _f32, _f32,
+                              _f32, _f32, _f32, _u64, _i64, _i32, _P, _P],
     "fn_params": [_u64, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _f32, _f32, _P, _P],
+    "fn_params_ex": [_u64, _i64, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _f32, _f32, _P, _P],
     "fn_test_erase_dims": [_P, _P, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _P, _P, _P, _P],
     "fn_test_cr_ops": [_i32, _P, _P, _i64, _P, _P],
     "fn_test_copy": [_P, _P, _i64, _P],
@@ -49,8 +52,8 @@ for _name, _args in _SIGS.items():
 _lib.fn_last_error.argtypes = []
 _lib.fn_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ("fn_fused_normalize", "fn_params", "fn_last_error", "fn_test_erase_dims",
-            "fn_test_cr_ops", "fn_test_copy")
+EXPORTED = ("fn_fused_normalize", "fn_fused_normalize_ex", "fn_params", "fn_params_ex",
+            "fn_last_error", "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_copy")
 
 
 class FnError(RuntimeError):
@@ -102,6 +105,22 @@ def fn_fused_normalize(in_u8, N, H, W, C, mean, std, flip_p, erase_p, scale_min,
         _addr(in_u8), N, H, W, C, _host_floats(mean, C), _host_floats(std, C), flip_p, erase_p,
         scale_min, scale_max, ratio_min, ratio_max, seed & 0xFFFFFFFFFFFFFFFF, out_dtype,
         _addr(out), _stream(stream)))
+
+
+def fn_fused_normalize_ex(in_u8, in_row_stride, in_image_stride, N, H, W, C, mean, std, flip_p,
+                          erase_p, scale_min, scale_max, ratio_min, ratio_max, seed,
+                          first_sample_id, out_dtype, out, stream=None) -> int:
+    return _check(_lib.fn_fused_normalize_ex(
+        _addr(in_u8), in_row_stride, in_image_stride, N, H, W, C, _host_floats(mean, C),
+        _host_floats(std, C), flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
+        seed & 0xFFFFFFFFFFFFFFFF, first_sample_id, out_dtype, _addr(out), _stream(stream)))
+
+
+def fn_params_ex(seed, first_sample_id, N, H, W, flip_p, erase_p, scale_min, scale_max,
+                 ratio_min, ratio_max, params_dev, stream=None) -> int:
+    return _check(_lib.fn_params_ex(seed & 0xFFFFFFFFFFFFFFFF, first_sample_id, N, H, W, flip_p,
+                                    erase_p, scale_min, scale_max, ratio_min, ratio_max,
+                                    _addr(params_dev), _stream(stream)))
 
 
 def fn_params(seed, N, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,

@@ -92,6 +92,7 @@ int make_draw_args(uint64_t seed, int32_t H, int32_t W, float flip_p, float eras
   if (!(ratio_min >= 0x1p-30f && ratio_min <= ratio_max && ratio_max <= 0x1p30f))
     return fail(FN_EINVAL, "need 2^-30 <= ratio_min <= ratio_max <= 2^30");
   a->seed = seed;
+  a->first_sample = 0;
   a->H = H;
   a->W = W;
   a->flip_p = flip_p;
@@ -241,8 +242,10 @@ void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, s
 // Tile plan of the tiles kernel: the largest tile of at most kTileBytesTarget
 // input bytes (whole rows, or whole images when one fits), shrunk -- down to
 // kMinTileBytes -- so that the batch gives every compute unit at least 8
-// tiles.  Sets the tile fields of `a`.
-int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elems, int cus) {
+// tiles.  row_slot > 0: strided rows, staged row_slot LDS bytes apart.
+// Sets the tile fields of `a`.
+int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elems, int cus,
+               int64_t row_slot) {
   int64_t target = fn::kTileBytesTarget;
   const int64_t want = (int64_t)cus * 8;
   if (elems / want < target) target = std::max<int64_t>(elems / want, fn::kMinTileBytes);
@@ -264,9 +267,13 @@ int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elem
     a->total_tiles = N * a->tiles_per_image;
     tile_bytes = r * row;
   }
-  if (tile_bytes > fn::kTileBytesMax) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
+  // contiguous: the tile's bytes plus the partial granules at both ends;
+  // strided: one 16-byte-granule slot per row
+  const int64_t tile_rows = a->images_per_tile == 1 ? a->rows_per_tile : a->images_per_tile * H;
+  const int64_t lds = row_slot > 0 ? tile_rows * row_slot : (tile_bytes + 32 + 15) / 16 * 16;
+  if (lds > fn::kTileBytesMax + 64) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
   if (a->total_tiles > 0x7FFFFFFF) return fail(FN_EOVERFLOW, "grid size limit exceeded");
-  a->lds_buffer_bytes = (int32_t)((tile_bytes + 32 + 15) / 16 * 16);
+  a->lds_buffer_bytes = (int32_t)lds;
   return FN_OK;
 }
 
@@ -284,14 +291,17 @@ void launch_grouped(const fn::FusedArgs& a, int C, int px, int out_dtype, unsign
 
 FN_EXPORT const char* fn_last_error(void) { return g_last_error.c_str(); }
 
-FN_EXPORT int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float flip_p,
-                        float erase_p, float scale_min, float scale_max, float ratio_min,
-                        float ratio_max, fn_sample_params* params_dev, void* stream) {
+FN_EXPORT int fn_params_ex(uint64_t seed, int64_t first_sample_id, int64_t N, int32_t H,
+                           int32_t W, float flip_p, float erase_p, float scale_min,
+                           float scale_max, float ratio_min, float ratio_max,
+                           fn_sample_params* params_dev, void* stream) {
   static_assert(sizeof(fn_sample_params) == sizeof(fn::SampleParams), "layout");
   fn::DrawArgs a;
   int rc = make_draw_args(seed, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
                           &a);
   if (rc) return rc;
+  if (first_sample_id < 0) return fail(FN_EINVAL, "first_sample_id must be >= 0");
+  a.first_sample = (uint64_t)first_sample_id;
   if (N < 0) return fail(FN_EINVAL, "N must be >= 0");
   if (N > ((int64_t)1 << 36)) return fail(FN_EOVERFLOW, "N too large");
   if (N == 0) return ok();
@@ -303,17 +313,30 @@ FN_EXPORT int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float fl
   return launch_status("params_kernel launch");
 }
 
-FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H, int32_t W,
-                                 int32_t C, const float* mean, const float* std, float flip_p,
-                                 float erase_p, float scale_min, float scale_max, float ratio_min,
-                                 float ratio_max, uint64_t seed, int32_t out_dtype, void* out_dev,
-                                 void* stream) {
+FN_EXPORT int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float flip_p,
+                        float erase_p, float scale_min, float scale_max, float ratio_min,
+                        float ratio_max, fn_sample_params* params_dev, void* stream) {
+  return fn_params_ex(seed, 0, N, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min,
+                      ratio_max, params_dev, stream);
+}
+
+namespace {
+
+// Both fused entry points.  strides == nullptr: the compact layout; else
+// {row stride, image stride} of the source in bytes.
+int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64_t N, int32_t H,
+                         int32_t W, int32_t C, const float* mean, const float* std, float flip_p,
+                         float erase_p, float scale_min, float scale_max, float ratio_min,
+                         float ratio_max, uint64_t seed, int64_t first_sample_id,
+                         int32_t out_dtype, void* out_dev, void* stream) {
   fn::FusedArgs a{};
   int rc = make_draw_args(seed, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
                           &a.draw);
   if (rc) return rc;
   if (C < 1 || C > 4) return fail(FN_EINVAL, "C must be in 1..4 (got %d)", C);
   if (N < 0) return fail(FN_EINVAL, "N must be >= 0");
+  if (first_sample_id < 0) return fail(FN_EINVAL, "first_sample_id must be >= 0");
+  a.draw.first_sample = (uint64_t)first_sample_id;
   if (out_dtype != FN_OUT_FP32 && out_dtype != FN_OUT_FP16 && out_dtype != FN_OUT_FP16_PAD4)
     return fail(FN_EINVAL, "unknown out_dtype %d", out_dtype);
   if (mean == nullptr || std == nullptr) return fail(FN_EINVAL, "mean and std must not be NULL");
@@ -325,12 +348,28 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
   const int64_t img = (int64_t)H * W * C;
   if (N > INT64_MAX / 16 / ((int64_t)H * W)) return fail(FN_EOVERFLOW, "N*H*W*4*4 overflows int64");
   const int64_t elems = N * img;
+  const int64_t row = (int64_t)W * C;
+  int64_t row_stride = row, image_stride = img;
+  if (strides != nullptr) {
+    row_stride = strides[0];
+    image_stride = strides[1];
+    if (row_stride < row) return fail(FN_EINVAL, "in_row_stride must be >= W*C");
+    if (image_stride < 0) return fail(FN_EINVAL, "in_image_stride must be >= 0");
+  }
+  // input bytes from the first one read to the last: (N-1) image strides,
+  // (H-1) row strides and one row
+  int64_t span = 0;
+  if (N > 0) {
+    const __int128 s128 = (__int128)(N - 1) * image_stride + (__int128)(H - 1) * row_stride + row;
+    if (s128 > (__int128)INT64_MAX / 2) return fail(FN_EOVERFLOW, "input span overflows int64");
+    span = (int64_t)s128;
+  }
+  const bool strided = row_stride != row || image_stride != img;
   const int out_bytes = out_dtype == FN_OUT_FP32 ? 4 : 2;
   const int oc = out_dtype == FN_OUT_FP16_PAD4 ? 4 : C;  // output channels per pixel
   const int64_t out_elems = N * H * (int64_t)W * oc;
 
   // generic kernel tiles: about 8 KiB of input, whole rows
-  const int64_t row = (int64_t)W * C;
   int64_t rows = (8192 + row - 1) / row;
   if (rows > H) rows = H;
   a.rows_per_tile = (int32_t)rows;
@@ -341,11 +380,11 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
 
   if ((uintptr_t)out_dev % (uintptr_t)out_bytes != 0)
     return fail(FN_EINVAL, "out_dev must be aligned to its element size (%d bytes)", out_bytes);
-  rc = check_device_range(in_u8_dev, (size_t)elems, "in_u8_dev");
+  rc = check_device_range(in_u8_dev, (size_t)span, "in_u8_dev");
   if (rc) return rc;
   rc = check_device_range(out_dev, (size_t)out_elems * out_bytes, "out_dev");
   if (rc) return rc;
-  const uintptr_t i0 = (uintptr_t)in_u8_dev, i1 = i0 + (uintptr_t)elems;
+  const uintptr_t i0 = (uintptr_t)in_u8_dev, i1 = i0 + (uintptr_t)span;
   const uintptr_t o0 = (uintptr_t)out_dev, o1 = o0 + (uintptr_t)out_elems * out_bytes;
   if (i0 < o1 && o0 < i1) return fail(FN_EINVAL, "input and output overlap");
 
@@ -367,15 +406,22 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
   }
 
   hipStream_t st = (hipStream_t)stream;
-  a.total_bytes = elems;
+  a.total_bytes = span;
+  a.in_row_stride = row_stride;
+  a.in_image_stride = image_stride;
+  a.strided = strided ? 1 : 0;
   const int64_t row_out = (int64_t)W * oc;
   if ((uintptr_t)out_dev % 16 == 0 && row_out % (16 / out_bytes) == 0 &&
       row <= fn::kTileBytesMax) {
     int cus = 0;
     rc = device_cu_count(&cus);
     if (rc) return rc;
-    rc = plan_tiles(&a, N, H, row, elems, cus);
+    // strided rows: one slot of whole 16-byte granules per row
+    const int64_t row_slot = strided ? (15 + row + 15) / 16 * 16 : 0;
+    rc = plan_tiles(&a, N, H, row, elems, cus, row_slot);
     if (rc) return rc;
+    a.row_slot = (int32_t)row_slot;
+    a.div_gps = make_fast_div((uint32_t)std::max<int64_t>(row_slot / 16, 1));
     a.div_row = make_fast_div((uint32_t)row);
     a.div_row_out = make_fast_div((uint32_t)row_out);
     a.div_h = make_fast_div((uint32_t)H);
@@ -383,7 +429,7 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
     launch_tiles(a, C, out_dtype, (unsigned)a.total_tiles, tiles_lds_bytes(a.lds_buffer_bytes), st);
     return launch_status("fused_tiles_kernel launch");
   }
-  const int px = out_dtype == FN_OUT_FP16_PAD4
+  const int px = out_dtype == FN_OUT_FP16_PAD4 || strided
                      ? 0
                      : pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);
   if (px > 0) {
@@ -413,6 +459,31 @@ FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H,
   else
     fn::fused_generic_kernel<_Float16><<<grid, fn::kBlock, 0, st>>>(a);
   return launch_status("fused_generic_kernel launch");
+}
+
+}  // namespace
+
+FN_EXPORT int fn_fused_normalize(const uint8_t* in_u8_dev, int64_t N, int32_t H, int32_t W,
+                                 int32_t C, const float* mean, const float* std, float flip_p,
+                                 float erase_p, float scale_min, float scale_max, float ratio_min,
+                                 float ratio_max, uint64_t seed, int32_t out_dtype, void* out_dev,
+                                 void* stream) {
+  return fused_normalize_impl(in_u8_dev, nullptr, N, H, W, C, mean, std, flip_p, erase_p,
+                              scale_min, scale_max, ratio_min, ratio_max, seed, 0, out_dtype,
+                              out_dev, stream);
+}
+
+FN_EXPORT int fn_fused_normalize_ex(const uint8_t* in_u8_dev, int64_t in_row_stride,
+                                    int64_t in_image_stride, int64_t N, int32_t H, int32_t W,
+                                    int32_t C, const float* mean, const float* std, float flip_p,
+                                    float erase_p, float scale_min, float scale_max,
+                                    float ratio_min, float ratio_max, uint64_t seed,
+                                    int64_t first_sample_id, int32_t out_dtype, void* out_dev,
+                                    void* stream) {
+  const int64_t strides[2] = {in_row_stride, in_image_stride};
+  return fused_normalize_impl(in_u8_dev, strides, N, H, W, C, mean, std, flip_p, erase_p,
+                              scale_min, scale_max, ratio_min, ratio_max, seed, first_sample_id,
+                              out_dtype, out_dev, stream);
 }
 
 FN_EXPORT int fn_test_erase_dims(const uint32_t* w_scale_dev, const uint32_t* w_ratio_dev,

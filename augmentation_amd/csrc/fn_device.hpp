@@ -215,6 +215,7 @@ __device__ __forceinline__ int32_t round_half_away(float s) {
 // ---------------------------------------------------------------------------
 struct DrawArgs {
   uint64_t seed;
+  uint64_t first_sample;     // sample n of a call draws from stream first_sample + n
   int32_t H, W;
   float flip_p, erase_p;
   float scale_min, scale_max;
@@ -269,7 +270,8 @@ __device__ __forceinline__ uint32_t from_lane_plus2(uint32_t x) {
 
 // ---------------------------------------------------------------------------
 // The decisions of one sample, computed by a group of 16 lanes (lanes
-// 16g .. 16g+15 of a wavefront draw for the sample their caller passes; a
+// 16g .. 16g+15 of a wavefront draw for the sample their caller passes --
+// stream a.first_sample + n; a
 // wavefront serves four samples at once).  Every lane of the wavefront must
 // make the call together; the group's first lane (16g) gets the result, the
 // other lanes' results are unspecified.
@@ -293,7 +295,7 @@ __device__ __forceinline__ SampleParams draw_sample_params16(const DrawArgs& a, 
   const int first_attempt_word = has_flip + 1;  // after the flip word and the gate word
   const int k = first_attempt_word + 2 * gl;
 
-  const Block4 own = stream_block(a.seed, n, (uint64_t)(k >> 2));
+  const Block4 own = stream_block(a.seed, a.first_sample + n, (uint64_t)(k >> 2));
   const uint32_t w0 = own.w[0];  // in the first lane: words 0 and 1 of the stream
   const uint32_t w_gate = has_flip ? own.w[1] : own.w[0];
 

@@ -105,7 +105,13 @@ struct FusedArgs {
   int32_t images_per_tile;
   int64_t total_tiles;
   int32_t lds_buffer_bytes;   // the LDS staging buffer of one tile
-  int64_t total_bytes;        // N * H * W * C
+  int64_t total_bytes;        // input bytes from the first to the last one read
+  // input rows: row h of image n starts at in + n * in_image_stride +
+  // h * in_row_stride; strided == 0 when that is the compact layout
+  int64_t in_row_stride, in_image_stride;
+  int32_t strided;
+  int32_t row_slot;           // strided tiles: LDS bytes per row (16 * granules)
+  FastDiv div_gps;            // by row_slot / 16
   FastDiv div_row;            // by W * C
   FastDiv div_row_out;        // by W * oc
   FastDiv div_h;              // by H
@@ -496,6 +502,49 @@ __device__ __forceinline__ void load_tile_waves(const FusedArgs& a, const Tile& 
   }
 }
 
+// First input byte of row r of tile T in a strided source.
+__device__ __forceinline__ uintptr_t tile_row_src(const FusedArgs& a, const Tile& T, int32_t r) {
+  uint32_t slot;
+  int32_t h;
+  tile_row_image(a, T, T.n_first, r, &slot, &h);
+  return (uintptr_t)a.in + (uintptr_t)(((int64_t)T.n_first + slot) * a.in_image_stride +
+                                       (int64_t)h * a.in_row_stride);
+}
+
+// The strided counterpart of load_tile_waves: row r of the tile is staged at
+// buf + r * row_slot, its first byte at offset head_r = (its address & 15).
+// Granule q of the tile is granule q mod gps of row q / gps (gps = row_slot
+// / 16) and lands at buf + 16 q, so a batch of 64 granules is still one DMA
+// per wavefront; granules past the end of a row are not read.
+__device__ __forceinline__ void load_tile_rows_waves(const FusedArgs& a, const Tile& T,
+                                                     uint8_t* buf, int32_t index,
+                                                     int32_t count) {
+  const int lane = (int)(threadIdx.x & 63u);
+  const uintptr_t in_lo = (uintptr_t)a.in, in_hi = in_lo + (uintptr_t)a.total_bytes;
+  const int32_t row = a.W * a.C;
+  const int32_t gps = a.row_slot >> 4;
+  const int32_t ngran = T.rows * gps;
+  for (int32_t batch = 64 * index; batch < ngran; batch += 64 * count) {
+    const int32_t q = batch + lane;
+    const int32_t r = (int32_t)fast_div((uint32_t)q, a.div_gps);
+    const int32_t g = q - r * gps;
+    const uintptr_t src = tile_row_src(a, T, min(r, T.rows - 1));
+    const int32_t head = (int32_t)(src & 15u);
+    const uintptr_t A = (src & ~(uintptr_t)15) + 16 * (uintptr_t)g;
+    const bool needed = q < ngran && 16 * g < head + row;
+    if (needed && A >= in_lo && A + 16 <= in_hi) {
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(A),
+                                       (__attribute__((address_space(3))) void*)(buf + 16 * batch),
+                                       16, 0, 0);
+    } else if (needed) {
+      for (int b = 0; b < 16; ++b) {
+        const uintptr_t addr = A + (uintptr_t)b;
+        if (addr >= in_lo && addr < in_hi) buf[16 * q + b] = *reinterpret_cast<const uint8_t*>(addr);
+      }
+    }
+  }
+}
+
 // Work-group size of the tiles kernel: 256 lanes for 8-element (fp16) chunks,
 // 512 for 4-element (fp32) chunks, so that a pass covers whole rows of
 // typical widths with few idle lanes.
@@ -534,12 +583,22 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
     const SampleParams p = draw_sample_params16(a.draw, (uint64_t)(T.n_first + slot));
     if ((threadIdx.x & 15u) == 0 && slot < n_count) s_params[slot] = p;
   }
-  if (wave >= load_first) load_tile_waves(a, T, s_lds, wave - load_first, kWaves - load_first);
+  if (wave >= load_first) {
+    if (a.strided)
+      load_tile_rows_waves(a, T, s_lds, wave - load_first, kWaves - load_first);
+    else
+      load_tile_waves(a, T, s_lds, wave - load_first, kWaves - load_first);
+  }
   __builtin_amdgcn_s_waitcnt(0);  // this wavefront's DMA loads have landed
   __syncthreads();
 
   const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
-  const int32_t row = a.W * C;        // input bytes of a row (as staged in LDS)
+  const int32_t row = a.W * C;        // input bytes of a row
+  // LDS offset of the first byte of tile row r
+  auto row_lds = [&](int32_t r) -> int32_t {
+    if (a.strided) return r * a.row_slot + (int32_t)(tile_row_src(a, T, r) & 15u);
+    return head + r * row;
+  };
   const int32_t row_out = a.W * OC;   // output elements of a row
   const int32_t cpr = row_out / E;    // chunks per row
   const int ct = (int)threadIdx.x;
@@ -556,7 +615,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       if (single) {
         for (int32_t r = slot_row; r < T.rows; r += rpi) {
           float v[E];
-          cs.values(s_lds, head + r * row, P0, T.h0 + r, v);
+          cs.values(s_lds, row_lds(r), P0, T.h0 + r, v);
           store_group<OutT, E>(out + (int64_t)r * row_out + cs.x0, v);
         }
       } else {
@@ -566,7 +625,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
           tile_row_image(a, T, T.n_first, r, &slot, &h);
           const SampleParams P = s_params[slot];
           float v[E];
-          cs.values(s_lds, head + r * row, P, h, v);
+          cs.values(s_lds, row_lds(r), P, h, v);
           store_group<OutT, E>(out + (int64_t)r * row_out + cs.x0, v);
         }
       }
@@ -583,7 +642,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       const SampleParams P = single ? P0 : s_params[slot];
       const Setup cq(a, x0);
       float v[E];
-      cq.values(s_lds, head + (int32_t)r * row, P, h, v);
+      cq.values(s_lds, row_lds((int32_t)r), P, h, v);
       store_group<OutT, E>(out + off, v);
     }
   }
@@ -599,11 +658,10 @@ __global__ void __launch_bounds__(kBlock) fused_generic_kernel(FusedArgs a) {
   const SampleParams p = s_params[0];
 
   const int32_t W = a.W, C = a.C, OC = a.oc;
-  const int64_t row_elems = (int64_t)W * C;  // input bytes of a row
   const int64_t row_out = (int64_t)W * OC;   // output elements of a row
   const int32_t h0 = tile * a.rows_per_tile;
   const int32_t h1 = min(a.H, h0 + a.rows_per_tile);
-  const int64_t img_base = n * (int64_t)a.H * row_elems;
+  const int64_t img_base = n * a.in_image_stride;
   const int64_t begin = (n * (int64_t)a.H + h0) * row_out;
   const int64_t count = (int64_t)(h1 - h0) * row_out;
   OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out);
@@ -617,7 +675,7 @@ __global__ void __launch_bounds__(kBlock) fused_generic_kernel(FusedArgs a) {
     float v = 0.0f;
     if (!erased && c < C) {
       const int32_t src_w = p.flip ? (W - 1 - w) : w;
-      const uint8_t x = a.in[img_base + (int64_t)h * row_elems + (int64_t)src_w * C + c];
+      const uint8_t x = a.in[img_base + (int64_t)h * a.in_row_stride + (int64_t)src_w * C + c];
       v = __builtin_fmaf((float)x, a.mul[c], a.nsub[c]);
     }
     out[begin + idx] = to_out<OutT>(v);

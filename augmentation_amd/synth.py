@@ -71,6 +71,12 @@ class Workload:
     scale: tuple = ERASE_SCALE
     ratio: tuple = ERASE_RATIO
     seeds: tuple = field(default=(PARAM_SEED,))  # one launch per seed, same input
+    # source images larger than H x W: the operation reads the H x W window
+    # at (y0, x0) of each src_h x src_w image (0: the source is H x W)
+    src_h: int = 0
+    src_w: int = 0
+    y0: int = 0
+    x0: int = 0
 
     @property
     def launches(self) -> int:
@@ -98,12 +104,22 @@ class Workload:
         read once and every output element written once, erased or not."""
         return self.elems + self.N * self.H * self.W * self.out_channels * self.out_bytes
 
+    @property
+    def source_shape(self) -> tuple:
+        return (self.N, self.src_h or self.H, self.src_w or self.W, self.C)
+
     def make_input(self) -> np.ndarray:
-        """The whole (N, H, W, C) uint8 batch, from the workload's data seed."""
+        """The whole source batch (N, src_h, src_w, C) uint8, from the
+        workload's data seed."""
         rng = np.random.default_rng(self.data_seed)
+        N, sh, sw, C = self.source_shape
         if self.kind == "gradient":
-            return gradient_images(rng, self.N, self.H, self.W, self.C)
-        return uniform_images(rng, self.N, self.H, self.W, self.C)
+            return gradient_images(rng, N, sh, sw, C)
+        return uniform_images(rng, N, sh, sw, C)
+
+    def window(self, x: np.ndarray) -> np.ndarray:
+        """The H x W windows the operation reads, as a compact array."""
+        return np.ascontiguousarray(x[:, self.y0:self.y0 + self.H, self.x0:self.x0 + self.W])
 
 
 WORKLOADS = {
@@ -115,6 +131,11 @@ WORKLOADS = {
                              0.0, 0.0, OUT_FP32, 1004),
     "stress": Workload("stress", 2048, 224, 224, 3, IMAGENET_MEAN, IMAGENET_STD, 0.5, 1.0,
                        OUT_FP16, 1005, seeds=tuple(range(PARAM_SEED, PARAM_SEED + 8))),
+    # the training batch read as centre 224x224 windows of 256x256 sources
+    # (the crop that precedes the fused step, page "(11)" section 4)
+    "imagenet_crop": Workload("imagenet_crop", 256, 224, 224, 3, IMAGENET_MEAN, IMAGENET_STD,
+                              0.5, 0.5, OUT_FP16, 1006, kind="gradient", src_h=256, src_w=256,
+                              y0=16, x0=16),
     # the training batch in the page's 4-channel mixed-precision layout (section 8)
     "imagenet_train_pad4": Workload("imagenet_train_pad4", 256, 224, 224, 3, IMAGENET_MEAN,
                                     IMAGENET_STD, 0.5, 0.5, OUT_FP16_PAD4, 1003, kind="gradient"),

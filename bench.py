@@ -130,10 +130,20 @@ def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -
     torch.cuda.synchronize()
     seeds = w.seeds
 
+    _, sh, sw, _ = w.source_shape
+    row_stride, image_stride = sw * w.C, sh * sw * w.C
+    first = (w.y0 * sw + w.x0) * w.C  # the window's first byte in each source image
+
     def launch(k):
-        b.fn_fused_normalize(ins[k], w.N, w.H, w.W, w.C, w.mean, w.std, w.flip_p, w.erase_p,
-                             w.scale[0], w.scale[1], w.ratio[0], w.ratio[1],
-                             seeds[k % len(seeds)], w.out_dtype, outs[k], stream)
+        if (sh, sw) == (w.H, w.W):
+            b.fn_fused_normalize(ins[k], w.N, w.H, w.W, w.C, w.mean, w.std, w.flip_p, w.erase_p,
+                                 w.scale[0], w.scale[1], w.ratio[0], w.ratio[1],
+                                 seeds[k % len(seeds)], w.out_dtype, outs[k], stream)
+        else:
+            b.fn_fused_normalize_ex(ins[k].data_ptr() + first, row_stride, image_stride, w.N,
+                                    w.H, w.W, w.C, w.mean, w.std, w.flip_p, w.erase_p,
+                                    w.scale[0], w.scale[1], w.ratio[0], w.ratio[1],
+                                    seeds[k % len(seeds)], 0, w.out_dtype, outs[k], stream)
 
     ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s)
     del ins, outs

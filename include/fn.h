@@ -136,6 +136,52 @@ int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float flip_p, floa
               float scale_min, float scale_max, float ratio_min, float ratio_max,
               fn_sample_params* params_dev, void* stream);
 
+/*
+ * fn_fused_normalize_ex -- fn_fused_normalize on a strided source, with the
+ * sample numbering offset.
+ *
+ *   in_u8_dev        the first byte read: channel 0 of pixel (0, 0) of image 0.
+ *   in_row_stride    bytes from one source row to the next, >= W*C.
+ *   in_image_stride  bytes from one source image to the next, >= 0 (images
+ *                    may overlap; 0 reads the same image N times).
+ *                    Row h of image n starts at
+ *                    in_u8_dev + n*in_image_stride + h*in_row_stride and
+ *                    holds W*C bytes.  With W*C and H*W*C this is
+ *                    fn_fused_normalize's layout.  The page's per-image
+ *                    entry point takes such a row stride (page sec. 5,
+ *                    execute(input_ptr, width, height, input_stride, ...)),
+ *                    and the crop that precedes the fused step in the
+ *                    operator chain (page sec. 4) is then a pointer offset:
+ *                    pass the window's top-left pixel and the full image's
+ *                    strides.
+ *   first_sample_id  >= 0; sample n of this call draws from stream
+ *                    (seed, first_sample_id + n) (page sec. 10: decisions
+ *                    are a function of seed and offset only).  Splitting a
+ *                    batch into slices [a, b) called with first_sample_id =
+ *                    a reproduces the whole batch's result bit for bit, on
+ *                    one device or several.
+ *   all other arguments as fn_fused_normalize; the output is compact.
+ *
+ * Errors: as fn_fused_normalize, plus FN_EINVAL for in_row_stride < W*C,
+ * in_image_stride < 0 or first_sample_id < 0, and FN_EOVERFLOW when the
+ * input span (N-1)*in_image_stride + (H-1)*in_row_stride + W*C exceeds
+ * 2^62.  The whole span must lie in one device allocation.
+ */
+int fn_fused_normalize_ex(const uint8_t* in_u8_dev, int64_t in_row_stride,
+                          int64_t in_image_stride, int64_t N, int32_t H, int32_t W, int32_t C,
+                          const float* mean, const float* std, float flip_p, float erase_p,
+                          float scale_min, float scale_max, float ratio_min, float ratio_max,
+                          uint64_t seed, int64_t first_sample_id, int32_t out_dtype,
+                          void* out_dev, void* stream);
+
+/* fn_params_ex -- fn_params for samples first_sample_id .. first_sample_id +
+ * N - 1: params_dev[n] is sample first_sample_id + n's record, the decisions
+ * fn_fused_normalize_ex takes with the same first_sample_id.  Errors as
+ * fn_params, plus FN_EINVAL for first_sample_id < 0. */
+int fn_params_ex(uint64_t seed, int64_t first_sample_id, int64_t N, int32_t H, int32_t W,
+                 float flip_p, float erase_p, float scale_min, float scale_max, float ratio_min,
+                 float ratio_max, fn_sample_params* params_dev, void* stream);
+
 /* The message of the last nonzero return on the calling thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
 const char* fn_last_error(void);

@@ -133,3 +133,31 @@ def test_product_path_does_not_touch_the_oracle():
     assert "fn_" not in re.sub(r"/\*.*?\*/", "", otext, flags=re.S)
     otext = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
     assert not re.search(r"^\s*(from|import)\s+augmentation_amd", otext, flags=re.M)
+
+
+def call_fused_ex(b, row_stride, image_stride, first_sample_id, **kw):
+    a = dict(DEFAULT, **kw)
+    C = a["C"]
+    return b._lib.fn_fused_normalize_ex(
+        None, row_stride, image_stride, a["N"], a["H"], a["W"], C, ctypes_floats(a["mean"], C),
+        ctypes_floats(a["std"], C), a["flip_p"], a["erase_p"], a["scale_min"], a["scale_max"],
+        a["ratio_min"], a["ratio_max"], a["seed"], first_sample_id, a["out_dtype"], None, None)
+
+
+@pytest.mark.parametrize("row_stride,image_stride,first,code", [
+    (23, 8 * 24, 0, -1),            # row stride below W*C = 24
+    (24, -1, 0, -1),                # negative image stride
+    (24, 8 * 24, -5, -1),           # negative first sample
+    (2**61, 0, 0, -2),              # (H-1) row strides overflow the span limit
+    (24, 2**61, 0, -2),             # (N-1) image strides overflow the span limit
+])
+def test_ex_invalid_strides_rejected(b, row_stride, image_stride, first, code):
+    assert call_fused_ex(b, row_stride, image_stride, first) == code
+    assert b.fn_last_error() != ""
+
+
+def test_ex_valid_layouts_accepted_without_launch(b):
+    for rs, ims, first in ((24, 8 * 24, 0), (100, 0, 0), (24, 8 * 24 + 3, 2**40), (31, 1000, 7)):
+        assert call_fused_ex(b, rs, ims, first, N=0) == 0, b.fn_last_error()
+    assert b._lib.fn_params_ex(1, -1, 4, 8, 8, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, None, None) == -1
+    assert b._lib.fn_params_ex(1, 5, 0, 8, 8, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, None, None) == 0

@@ -47,11 +47,29 @@ def ulp16(ref: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(a)) - 10)
 
 
-def check_values(got: np.ndarray, ref: np.ndarray, what: str, rne_exact: bool = True) -> dict:
+def erased_mask(P: np.ndarray, H: int, W: int) -> np.ndarray:
+    """(N, H, W, 1) bool: pixels inside each sample's erase rectangle."""
+    h = np.arange(H)[None, :, None]
+    w = np.arange(W)[None, None, :]
+    e = P["erase"][:, None, None].astype(bool)
+    i, j = P["i"][:, None, None], P["j"][:, None, None]
+    eh, ew = P["eh"][:, None, None], P["ew"][:, None, None]
+    return (e & (h >= i) & (h < i + eh) & (w >= j) & (w < j + ew))[..., None]
+
+
+def check_values(got: np.ndarray, ref: np.ndarray, what: str, rne_exact: bool = True,
+                 erased: np.ndarray | None = None) -> dict:
     """Compare a GPU output (fp32 or fp16) with the oracle's fp32 result.
-    rne_exact: fp16 must equal RNE16(oracle) everywhere (preset constants)."""
+    rne_exact: fp16 must equal RNE16(oracle) everywhere (preset constants).
+    erased: elements that must be exactly +0; by default the elements where
+    the oracle is +0 (no normalized value is exactly 0 at the preset
+    constants, so there the two coincide).
+    Bounds: fp32 within FP32_TOL of the oracle (the fma's and constants'
+    roundings); fp16 output is RNE16 of that fp32 value, so within
+    max(1 ulp, FP32_TOL + 1/2 ulp) of the oracle -- the second term only
+    matters within ~0.004 of 0, where a value can cancel exactly."""
     assert got.shape == ref.shape, what
-    zero = ref.view(np.uint32) == 0
+    zero = ref.view(np.uint32) == 0 if erased is None else np.broadcast_to(erased, ref.shape)
     if got.dtype == np.float32:
         err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
         assert float(err.max(initial=0.0)) <= FP32_TOL, (what, float(err.max()))
@@ -59,7 +77,8 @@ def check_values(got: np.ndarray, ref: np.ndarray, what: str, rne_exact: bool = 
         return {"max_abs": float(err.max(initial=0.0))}
     assert got.dtype == np.float16
     err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
-    bad = err > ulp16(ref)
+    u = ulp16(ref)
+    bad = err > np.maximum(u, FP32_TOL + 0.5 * u)
     assert not np.any(bad), (what, int(bad.sum()), float(err.max()))
     assert np.all(got.view(np.uint16)[zero] == 0), what
     same = float(np.mean(got.view(np.uint16) == ref.astype(np.float16).view(np.uint16)))
