@@ -120,6 +120,21 @@ def time_launches(launch, steps: int, warmup: int, sets: int, stream, prewarm_s:
     return start.elapsed_time(end) / steps
 
 
+def median_call_ms(launch, calls: int, sets: int, stream) -> float:
+    """Median over `calls` individually timed launches (an event pair around
+    each; untimed, after the main measurement)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for k, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        launch(k % sets)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return times[len(times) // 2]
+
+
 def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -> dict:
     import torch
     stream = torch.cuda.current_stream()
@@ -146,9 +161,10 @@ def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -
                                     seeds[k % len(seeds)], 0, w.out_dtype, outs[k], stream)
 
     ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s)
+    med = median_call_ms(launch, min(steps, 200), sets, stream)
     del ins, outs
     torch.cuda.empty_cache()
-    return {"ms": ms, "images_per_s": w.N / (ms * 1e-3),
+    return {"ms": ms, "median_call_ms": med, "images_per_s": w.N / (ms * 1e-3),
             "gbs": w.nominal_bytes / (ms * 1e-3) / 1e9}
 
 
@@ -173,7 +189,8 @@ def bench_copy(b, nbytes: int, steps: int, warmup: int, sets: int, prewarm_s: fl
 
 def cpu_baseline(w, budget_s: float) -> dict:
     """The oracle as it stands, on this host's cores, over whole batches of
-    the workload (fp32 output) until about budget_s seconds have passed."""
+    the workload (fp32 output) until about budget_s seconds have passed;
+    then on one thread over a few images for about a fifth of that."""
     import oracle
     threads = host_threads()
     x = w.make_input()
@@ -186,10 +203,20 @@ def cpu_baseline(w, budget_s: float) -> dict:
         if el >= budget_s:
             break
     ips = reps * w.N / el
+    one, t1 = 0, time.perf_counter()
+    while True:
+        n = one % w.N
+        oracle.fused_normalize(x[n:n + 8], w.mean, w.std, w.flip_p, w.erase_p, w.scale, w.ratio,
+                               seed=w.seeds[0], first_n=n, threads=1)
+        one += 8
+        el1 = time.perf_counter() - t1
+        if el1 >= budget_s / 5:
+            break
     return {"value": round(ips, 2), "unit": "images/s", "cores": used, "kind": "oracle",
             "sample": f"{reps} x the {w.N}-image {w.H}x{w.W}x{w.C} batch, fp32 output, "
                       f"{used} threads, {el:.1f} s wall; CPU: {cpu_model()}",
-            "gbs_nominal": round(ips * w.H * w.W * w.C * (1 + 4) / 1e9, 3)}
+            "gbs_nominal": round(ips * w.H * w.W * w.C * (1 + 4) / 1e9, 3),
+            "single_thread_images_per_s": round(one / el1, 2)}
 
 
 def main() -> int:
@@ -244,7 +271,10 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),
+                     "traffic_gbs": (round(traffic["bytes_per_launch"] / (r["ms"] * 1e-3) / 1e9, 1)
+                                     if traffic else None),
                      "bytes_per_launch": w.nominal_bytes},
+        "median_call_ms": round(r["median_call_ms"], 5),
     }
     if not args.no_copy:
         c = bench_copy(b, w.nominal_bytes, args.steps, args.warmup, args.sets, args.prewarm_seconds)
