@@ -36,8 +36,9 @@ namespace fn {
 // Build-time tuning of the grouped kernel:
 //   FN_GROUP_PX_MAX  widest pixel group tried (16, 8 or 4)
 //   FN_GROUP_ITER    pixel groups per lane (1..4)
-//   FN_NT_STORE      output stores: 0 default, 1 non-temporal, 2 streaming
-//                    system-scope (sc0 sc1 nt)
+// and of the tiles kernel's lane-contiguous stores:
+//   FN_NT_STORE      0 default, 1 non-temporal, 2 streaming system-scope
+//                    (sc0 sc1 nt)
 #ifndef FN_GROUP_PX_MAX
 #define FN_GROUP_PX_MAX 16
 #endif
@@ -327,8 +328,8 @@ struct Tile {
   int64_t n_first;  // first image
   int32_t h0;       // first row in that image
   int32_t rows;     // rows in the tile (across images when several)
-  int64_t start;    // first input byte / output element
-  int32_t len;      // input bytes = output elements
+  int64_t start;    // offset of the tile's first byte in the compact layout
+  int32_t len;      // bytes of the tile in the compact layout (rows * W * C)
 };
 
 __device__ __forceinline__ Tile tile_at(const FusedArgs& a, uint32_t t) {
@@ -561,10 +562,11 @@ constexpr int tiles_threads() {
 // 16-lane group per image) while the other wavefronts DMA the tile into LDS
 // (when every wavefront draws, all of them load afterwards).  After one
 // barrier every lane makes E = 16/sizeof(OutT) consecutive output elements
-// of a row at a time and stores them as one 16-byte vector, lane-contiguous
-// across the wavefront.  Many small independent work-groups per compute unit
-// hide the memory latency.  Requires W*C a multiple of E and a 16-byte
-// aligned output.
+// of a row at a time (two whole 4-channel pixels when kPad4) and stores them
+// as one 16-byte vector, lane-contiguous across the wavefront.  Many small
+// independent work-groups per compute unit hide the memory latency.
+// Requires W*OC a multiple of E (OC = 4 when kPad4, else C) and a 16-byte
+// aligned output; the input may be compact or strided (a.strided).
 template <int C, typename OutT, bool kPad4>
 __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(FusedArgs a) {
   constexpr int kThreads = tiles_threads<OutT>();

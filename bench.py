@@ -16,7 +16,7 @@ Prints ONE JSON line:
              launches on the launch stream, against the 8 TB/s HBM peak;
              traffic = hardware bytes per launch from the committed
              rocprofv3 counter summary, if it was taken on the current
-             kernel source (else null)
+             build of libfn.so (else null)
   cpu_baseline  the oracle (plain C loops, fp32 output) timed on this
              host's cores over a bounded sample of the same workload.
 
@@ -43,22 +43,23 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fused_tiles_kernel_imagenet_train_counters.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "augmentation_amd", "csrc", f)
-                  for f in ("fn_api.hip", "fn_kernels.hpp", "fn_device.hpp", "exp2_table.inc")]
+LIBRARY = os.path.join(ROOT, "augmentation_amd", "libfn.so")
 
 
-def kernel_source_hash() -> str:
+def library_hash() -> str:
+    """SHA-256 (first 16 hex digits) of the built library: the kernels and
+    the host planning that launches them.  The build is deterministic, so
+    source edits that change no code (comments) keep the hash."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    with open(LIBRARY, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def counter_traffic() -> dict | None:
     """Hardware bytes per launch from the committed counter summary, or None
-    if it is missing or was taken on other kernel sources."""
-    if not os.path.exists(PROFILE_COUNTERS):
+    if it is missing or was taken on another build of the library."""
+    if not os.path.exists(PROFILE_COUNTERS) or not os.path.exists(LIBRARY):
         return None
     kv = {}
     with open(PROFILE_COUNTERS) as f:
@@ -66,7 +67,7 @@ def counter_traffic() -> dict | None:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("library_sha256") != library_hash():
         return None
     try:
         return {"bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
