@@ -346,3 +346,61 @@ def test_copy_hook(b):
     b.fn_test_copy(src, dst, n)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_batch_beyond_4gib(b):
+    """An input of more than 2^32 bytes (28,700 images of 224x224x3, fp16
+    output 8.6 GB): every decision checked, and the images on both sides of
+    the 4 GiB input boundary, the first and the last element by element --
+    32-bit offset arithmetic anywhere would show here.  The input is drawn
+    on the GPU from a seeded generator; sampled images are copied back."""
+    N, H, W, C = 28700, 224, 224, 3
+    img = H * W * C
+    assert N * img > 2**32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    say(f"beyond 4 GiB: {N} images, {N * img / 2**30:.2f} GiB input")
+    x = torch.randint(0, 256, (N, H, W, C), dtype=torch.uint8, device="cuda", generator=g)
+    out = torch.empty((N, H, W, C), dtype=torch.float16, device="cuda")
+    kw = dict(mean=synth.IMAGENET_MEAN, std=synth.IMAGENET_STD, flip_p=0.5, erase_p=0.5,
+              scale=synth.ERASE_SCALE, ratio=synth.ERASE_RATIO)
+    run_fused(b, x, N, H, W, C, kw, 999, 1, out)
+    t = b.sample_params(N, H, W, 0.5, 0.5, synth.ERASE_SCALE, synth.ERASE_RATIO, 999)
+    torch.cuda.synchronize()
+    P = oracle.params(999, 0, N, H, W, 0.5, 0.5, synth.ERASE_SCALE, synth.ERASE_RATIO)
+    assert b.params_to_numpy(t).tobytes() == P.tobytes()
+    boundary = 2**32 // img
+    picks = [0, boundary - 1, boundary, boundary + 1, N - 1]
+    idx = torch.tensor(picks, device="cuda")
+    xs = x.index_select(0, idx).cpu().numpy()
+    got = out.index_select(0, idx).cpu().numpy()
+    del x, out
+    torch.cuda.empty_cache()
+    for k, n in enumerate(picks):
+        ref, _ = oracle.fused_normalize(xs[k:k + 1], kw["mean"], kw["std"], 0.5, 0.5,
+                                        seed=999, first_n=n)
+        check_values(got[k:k + 1], ref, f"beyond 4 GiB, image {n}")
+
+
+def test_graph_capture_replays_match_eager(b):
+    """The call allocates nothing and issues no memset, so it can be captured
+    in a HIP graph: five replays, with eager work and synchronisations
+    between them, each equal to the eager result bit for bit."""
+    w = synth.WORKLOADS["cifar"]
+    xt = torch.from_numpy(w.make_input()).cuda()
+    eager = run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), 11, 1)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), 11, 1, out, stream=s)
+    torch.cuda.synchronize()
+    for k in range(5):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), k
+        _ = (xt.float() * 2).sum().item()  # unrelated eager work between replays
