@@ -506,8 +506,12 @@ __device__ __forceinline__ void load_tile_waves(const FusedArgs& a, const Tile& 
   }
 }
 
-// First input byte of row r of tile T in a strided source.
+// First input byte of row r of tile T in a strided source.  A tile of one
+// image is a base plus r row strides.
 __device__ __forceinline__ uintptr_t tile_row_src(const FusedArgs& a, const Tile& T, int32_t r) {
+  if (a.images_per_tile == 1)
+    return (uintptr_t)a.in + (uintptr_t)(T.n_first * a.in_image_stride +
+                                         (int64_t)(T.h0 + r) * a.in_row_stride);
   uint32_t slot;
   int32_t h;
   tile_row_image(a, T, T.n_first, r, &slot, &h);
