@@ -404,3 +404,27 @@ def test_graph_capture_replays_match_eager(b):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), k
         _ = (xt.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_concurrent_calls_on_two_streams(b):
+    """The library keeps no per-call state on the device: two calls with
+    different seeds and output types, enqueued on two streams and free to
+    overlap, each equal their own serial result."""
+    w = synth.WORKLOADS["imagenet_train"]
+    xt = torch.from_numpy(w.make_input()[:128]).cuda()
+    N = xt.shape[0]
+    ref16 = run_fused(b, xt, N, w.H, w.W, w.C, wl_dict(w), 5, 1)
+    ref32 = run_fused(b, xt, N, w.H, w.W, w.C, wl_dict(w), 6, 0)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    o16 = torch.empty_like(ref16)
+    o32 = torch.empty_like(ref32)
+    for _ in range(3):
+        o16.fill_(float("nan"))
+        o32.fill_(float("nan"))
+        torch.cuda.synchronize()
+        run_fused(b, xt, N, w.H, w.W, w.C, wl_dict(w), 5, 1, o16, stream=s1)
+        run_fused(b, xt, N, w.H, w.W, w.C, wl_dict(w), 6, 0, o32, stream=s2)
+        torch.cuda.synchronize()
+        assert torch.equal(o16.view(torch.int16), ref16.view(torch.int16))
+        assert torch.equal(o32.view(torch.int32), ref32.view(torch.int32))
