@@ -173,7 +173,10 @@ def test_stress_eight_back_to_back_launches(b):
 EDGE_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1, 3),
                (1, 1, 17, 3), (5, 17, 1, 3), (3, 2, 2, 1), (2, 31, 33, 3), (7, 13, 11, 4),
                (2, 4, 8192, 1), (1, 600, 6, 3), (9, 28, 28, 1), (64, 32, 32, 3),
-               (2, 3, 1024, 3), (2, 5, 700, 4), (40, 8, 8, 2), (3, 64, 48, 3)]
+               (2, 3, 1024, 3), (2, 5, 700, 4), (40, 8, 8, 2), (3, 64, 48, 3),
+               # rows wider than the largest LDS tile (24 KB): the pixel-group
+               # kernel (W a multiple of 8) and the element-wise one
+               (1, 3, 9000, 3), (1, 2, 9001, 3)]
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES)
