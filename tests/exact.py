@@ -51,3 +51,29 @@ def normalize_lut(mean, std) -> np.ndarray:
     C = len(mean)
     return np.array([[normalize_f32(x, mean[c], std[c]) for c in range(C)] for x in range(256)],
                     dtype=np.float32)
+
+
+def nearest_f64(q: Fraction) -> float:
+    """The double nearest to q (CPython's int / int division rounds
+    correctly, ties to even)."""
+    return q.numerator / q.denominator
+
+
+def sqrt_exact(q: Fraction, digits: int = 60) -> Fraction:
+    """sqrt(q) to `digits` significant digits (far more than any rounding
+    below needs; the square root of a float is never a rounding midpoint of
+    fp32 or fp64, so the nearest value is decided by these digits)."""
+    with localcontext() as ctx:
+        ctx.prec = digits
+        v = (Decimal(q.numerator) / Decimal(q.denominator)).sqrt()
+    return Fraction(v)
+
+
+def sqrt_f32(q: Fraction) -> np.float32:
+    """RN32(sqrt(q))."""
+    return nearest_f32(sqrt_exact(q))
+
+
+def round_half_away(q: Fraction) -> int:
+    """Nearest integer to q >= 0, halves away from zero."""
+    return int((q + Fraction(1, 2)).__floor__())

@@ -20,7 +20,7 @@ from conftest import ROOT
 import oracle
 
 PIN_FILES = ["test_oracle_philox.py", "test_oracle_math.py", "test_oracle_sampler.py",
-             "test_oracle_pixels.py"]
+             "test_oracle_rounding.py", "test_oracle_pixels.py"]
 
 # (name, original text, planted text)
 MUTANTS = [
@@ -52,6 +52,17 @@ MUTANTS = [
      "float v = (float)x * (1.0f / (255.0f * std[c]));\n                    out[o] = v - mean[c] / std[c];"),
     ("exp_truncated", "return (float)expl((long double)L);", "return nextafterf((float)expl((long double)L), 0.0f);"),
     ("log_ratio_fp32_libm", "return (float)logl((long double)r);", "return nextafterf((float)logl((long double)r), 0.0f);"),
+    # the rounding sequence of one attempt (page section 10 uniform(), section 12)
+    ("fma_area_fraction", "float scale_draw = or_u01(w_scale) * scale_span;\n    float target_fraction = scale_min + scale_draw;",
+     "float target_fraction = fmaf(or_u01(w_scale), scale_span, scale_min);"),
+    ("fma_log_aspect", "float log_draw = or_u01(w_ratio) * log_span;\n    float log_aspect = log_rmin + log_draw;",
+     "float log_aspect = fmaf(or_u01(w_ratio), log_span, log_rmin);"),
+    ("sqrt_in_double", "float side_h = sqrtf(erase_area * aspect);\n    float side_w = sqrtf(erase_area / aspect);",
+     "float side_h = (float)sqrt((double)erase_area * (double)aspect);\n    float side_w = (float)sqrt((double)erase_area / (double)aspect);"),
+    ("lerp_two_products", "float target_fraction = scale_min + scale_draw;",
+     "float target_fraction = scale_min * (1.0f - or_u01(w_scale)) + scale_max * or_u01(w_scale);\n    (void)scale_draw;"),
+    ("exponent_in_extended", "float aspect = or_expf(log_aspect);",
+     "float aspect = (float)expl((long double)log_rmin + (long double)or_u01(w_ratio) * ((long double)log_rmax - (long double)log_rmin));\n    (void)log_aspect;"),
 ]
 
 
