@@ -218,25 +218,82 @@ void launch_grouped_px(const fn::FusedArgs& a, int C, int out_dtype, unsigned gr
   }
 }
 
-template <int C>
+template <int C, bool kComp>
 void launch_tiles_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t lds,
                     hipStream_t st) {
   if (out_dtype == FN_OUT_FP32)
-    fn::fused_tiles_kernel<C, float, false><<<grid, fn::tiles_threads<float>(), lds, st>>>(a);
+    fn::fused_tiles_kernel<C, float, false, kComp>
+        <<<grid, fn::tiles_threads<float>(), lds, st>>>(a);
   else if (out_dtype == FN_OUT_FP16_PAD4)
-    fn::fused_tiles_kernel<C, _Float16, true><<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
+    fn::fused_tiles_kernel<C, _Float16, true, kComp>
+        <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
   else
-    fn::fused_tiles_kernel<C, _Float16, false><<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
+    fn::fused_tiles_kernel<C, _Float16, false, kComp>
+        <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
 }
 
-void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
-                  hipStream_t st) {
+template <bool kComp>
+void launch_tiles_k(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
+                    hipStream_t st) {
   switch (C) {
-    case 1: launch_tiles_c<1>(a, out_dtype, grid, lds, st); break;
-    case 2: launch_tiles_c<2>(a, out_dtype, grid, lds, st); break;
-    case 3: launch_tiles_c<3>(a, out_dtype, grid, lds, st); break;
-    default: launch_tiles_c<4>(a, out_dtype, grid, lds, st); break;
+    case 1: launch_tiles_c<1, kComp>(a, out_dtype, grid, lds, st); break;
+    case 2: launch_tiles_c<2, kComp>(a, out_dtype, grid, lds, st); break;
+    case 3: launch_tiles_c<3, kComp>(a, out_dtype, grid, lds, st); break;
+    default: launch_tiles_c<4, kComp>(a, out_dtype, grid, lds, st); break;
   }
+}
+
+void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, bool comp, unsigned grid,
+                  size_t lds, hipStream_t st) {
+  if (comp)
+    launch_tiles_k<true>(a, C, out_dtype, grid, lds, st);
+  else
+    launch_tiles_k<false>(a, C, out_dtype, grid, lds, st);
+}
+
+// Bits of the binary16 value nearest to v (ties to even), as the GPU's
+// float-to-half conversion gives them.
+uint16_t half_bits_rne(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);   // NaN
+  if (mag >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);  // at or beyond 65520: infinity
+  if (mag >= 0x38800000u) {                                   // normal: 2^-14 and up
+    const uint32_t m = mag - 0x38000000u;                     // exponent rebiased 127 -> 15
+    return (uint16_t)(sign | ((m + 0x0FFFu + ((m >> 13) & 1u)) >> 13));
+  }
+  // subnormal or zero: units of 2^-24, scaling by 2^24 is exact
+  const float units = std::nearbyint(std::fabs(v) * 0x1p24f);  // default rounding: ties to even
+  return (uint16_t)(sign | (uint32_t)units);
+}
+
+uint32_t float_bits(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  return u;
+}
+
+// True if one fma per element, fma(x, mul, nsub), stores exactly what the
+// two-fma form fma(x, mul, nsub) + fma(x, mul_lo, nsub_lo) stores, for every
+// byte value x of every channel: the fp32 bits, or the binary16 bits of
+// their rounding.  The inputs are bytes, so this covers every element the
+// kernel can meet.
+bool single_fma_exact(const fn::FusedArgs& a, int C, int out_dtype) {
+  for (int c = 0; c < C; ++c) {
+    for (int x = 0; x < 256; ++x) {
+      const float xf = (float)x;
+      const float one = std::fma(xf, a.mul[c], a.nsub[c]);
+      const float two = one + std::fma(xf, a.mul_lo[c], a.nsub_lo[c]);
+      if (out_dtype == FN_OUT_FP32) {
+        if (float_bits(one) != float_bits(two)) return false;
+      } else if (half_bits_rne(one) != half_bits_rne(two)) {
+        return false;
+      }
+    }
+  }
+  return true;
 }
 
 // Tile plan of the tiles kernel: the largest tile of at most kTileBytesTarget
@@ -395,13 +452,17 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
   a.W = W;
   a.C = C;
   a.oc = oc;
+  // 1/(255 std_c) and -mean_c/std_c, each rounded once to double and split
+  // into an fp32 pair hi + lo (the difference is exact in double)
   for (int c = 0; c < 4; ++c) {
+    a.mul[c] = a.mul_lo[c] = a.nsub[c] = a.nsub_lo[c] = 0.0f;
     if (c < C) {
-      a.mul[c] = (float)(1.0 / (255.0 * (double)std[c]));
-      a.nsub[c] = -(float)((double)mean[c] / (double)std[c]);
-    } else {
-      a.mul[c] = 0.0f;
-      a.nsub[c] = 0.0f;
+      const double m = 1.0 / (255.0 * (double)std[c]);
+      const double n = -((double)mean[c] / (double)std[c]);
+      a.mul[c] = (float)m;
+      a.mul_lo[c] = (float)(m - (double)a.mul[c]);
+      a.nsub[c] = (float)n;
+      a.nsub_lo[c] = (float)(n - (double)a.nsub[c]);
     }
   }
 
@@ -426,7 +487,9 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
     a.div_row_out = make_fast_div((uint32_t)row_out);
     a.div_h = make_fast_div((uint32_t)H);
     a.div_tpi = make_fast_div((uint32_t)a.tiles_per_image);
-    launch_tiles(a, C, out_dtype, (unsigned)a.total_tiles, tiles_lds_bytes(a.lds_buffer_bytes), st);
+    const bool comp = !single_fma_exact(a, C, out_dtype);
+    launch_tiles(a, C, out_dtype, comp, (unsigned)a.total_tiles,
+                 tiles_lds_bytes(a.lds_buffer_bytes), st);
     return launch_status("fused_tiles_kernel launch");
   }
   const int px = out_dtype == FN_OUT_FP16_PAD4 || strided

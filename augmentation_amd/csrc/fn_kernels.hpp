@@ -18,7 +18,8 @@
 //                          wholly inside the erase rectangle reads nothing.
 //   fused_generic_kernel   the same operation for any shape and alignment,
 //                          one element at a time.
-//   Values are one fma each, stored as fp32 or round-to-nearest-even fp16.
+//   Values are (x/255 - mean)/std from fp32 constant pairs (see
+//   normalize()), stored as fp32 or round-to-nearest-even fp16.
 //   erase_dims_kernel,
 //   cr_ops_kernel,
 //   copy_kernel            test and measurement hooks.
@@ -117,10 +118,29 @@ struct FusedArgs {
   FastDiv div_row_out;        // by W * oc
   FastDiv div_h;              // by H
   FastDiv div_tpi;            // by tiles_per_image
-  float mul[4];               // RN32(1 / (255 std_c))
-  float nsub[4];              // -RN32(mean_c / std_c)
+  // 1 / (255 std_c) = mul + mul_lo and -mean_c / std_c = nsub + nsub_lo,
+  // each the double value split into an fp32 pair (see normalize())
+  float mul[4], mul_lo[4];
+  float nsub[4], nsub_lo[4];
   DrawArgs draw;
 };
+
+// (x/255 - mean)/std of one byte x from the constant pairs m = mh + ml
+// (1/(255 std)) and n = nh + nl (-mean/std).  The first fma holds the part
+// where x*m and n cancel exactly inside one rounding; the second adds the
+// low parts.  The result is within about one fp32 ulp of the exact value
+// relative to the result itself, also where the value is near zero (one fma
+// on rounded constants errs there by up to ~1e-7 absolute, several fp16
+// ulps of a tiny result).
+// kComp false: the first fma alone.  The host takes that form only after
+// checking, for every byte value of every channel, that it yields exactly
+// the stored output of the two-fma form (see single_fma_exact in
+// fn_api.hip), so both forms write the same bits.
+template <bool kComp = true>
+__device__ __forceinline__ float normalize(float x, float mh, float ml, float nh, float nl) {
+  if constexpr (kComp) return __builtin_fmaf(x, mh, nh) + __builtin_fmaf(x, ml, nl);
+  return __builtin_fmaf(x, mh, nh);
+}
 
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kBlock) params_kernel(DrawArgs a, int64_t N,
@@ -246,7 +266,7 @@ __device__ __forceinline__ void group_values(const uint32_t (&w)[PX * C / 4], ui
         case 2: x = (float)((w[(sp * C + c) >> 2] >> 16) & 0xFFu); break;
         default: x = (float)(w[(sp * C + c) >> 2] >> 24); break;
       }
-      float y = __builtin_fmaf(x, a.mul[c], a.nsub[c]);
+      float y = normalize(x, a.mul[c], a.mul_lo[c], a.nsub[c], a.nsub_lo[c]);
       if (kMasked) y = ((erased >> p) & 1u) ? 0.0f : y;
       v[p * C + c] = y;
     }
@@ -363,6 +383,9 @@ __device__ __forceinline__ void tile_row_image(const FusedArgs& a, const Tile& T
   }
 }
 
+// How a lane reads its source bytes from LDS (see ChunkSetup::values).
+constexpr int kSrcAny = -1, kSrcFlip = 0, kSrcAligned = 1, kSrcBytes = 2;
+
 // ---------------------------------------------------------------------------
 // What one lane needs to turn the E elements of a row starting at element
 // x0 into outputs, independent of the row: the channel of each element and
@@ -370,10 +393,10 @@ __device__ __forceinline__ void tile_row_image(const FusedArgs& a, const Tile& T
 // sources.  Element x = w*C + c takes byte (W-1-w)*C + c when flipped; with
 // x0 = w0*C + c0 and rc_k = (c0 + k) mod C that byte is
 // (W-1-w0)*C - c0 - k + 2 rc_k.
-template <int C, int E>
+template <int C, int E, bool kComp>
 struct ChunkSetup {
   int32_t x0;
-  float mul[C], nsub[C];  // rotated: element k uses index k % C
+  float mul[C], mul_lo[C], nsub[C], nsub_lo[C];  // rotated: element k uses index k % C
   int32_t mirror[E];      // mirrored source byte of element k, from the row start
 
   __device__ __forceinline__ ChunkSetup(const FusedArgs& a, int32_t first) : x0(first) {
@@ -385,14 +408,18 @@ struct ChunkSetup {
       int32_t cj = c0 + j;
       cj = cj >= C ? cj - C : cj;
       rc[j] = cj;
-      float m = a.mul[0], s = a.nsub[0];
+      float m = a.mul[0], ml = a.mul_lo[0], s = a.nsub[0], sl = a.nsub_lo[0];
 #pragma unroll
       for (int cc = 1; cc < C; ++cc) {
         m = cj == cc ? a.mul[cc] : m;
+        ml = cj == cc ? a.mul_lo[cc] : ml;
         s = cj == cc ? a.nsub[cc] : s;
+        sl = cj == cc ? a.nsub_lo[cc] : sl;
       }
       mul[j] = m;
+      mul_lo[j] = ml;
       nsub[j] = s;
+      nsub_lo[j] = sl;
     }
     const int32_t base = (a.W - 1 - w0) * C - c0;
 #pragma unroll
@@ -400,15 +427,21 @@ struct ChunkSetup {
   }
 
   // Outputs of this lane's E elements of one row (LDS row start `row_lds`,
-  // image row h, the image's decisions P).
+  // image row h, the image's decisions P).  kSrc says how the source bytes
+  // are read: kSrcFlip mirrored bytes (P.flip set), kSrcAligned two dwords
+  // (row_lds + x0 4-byte aligned), kSrcBytes single bytes; kSrcAny decides
+  // per call.
+  template <int kSrc = kSrcAny>
   __device__ __forceinline__ void values(const uint8_t* s_tile, int32_t row_lds,
                                          const SampleParams& P, int32_t h, float (&v)[E]) const {
     float x[E];
     const int32_t src = row_lds + x0;
-    if (P.flip) {
+    const int mode = kSrc != kSrcAny ? kSrc : (P.flip ? kSrcFlip : ((src & 3) == 0 ? kSrcAligned
+                                                                                  : kSrcBytes));
+    if (mode == kSrcFlip) {
 #pragma unroll
       for (int k = 0; k < E; ++k) x[k] = (float)s_tile[row_lds + mirror[k]];
-    } else if ((src & 3) == 0) {
+    } else if (mode == kSrcAligned) {
       uint32_t wv[E / 4];
 #pragma unroll
       for (int q = 0; q < E / 4; ++q) wv[q] = reinterpret_cast<const uint32_t*>(s_tile + src)[q];
@@ -419,7 +452,8 @@ struct ChunkSetup {
       for (int k = 0; k < E; ++k) x[k] = (float)s_tile[src + k];
     }
 #pragma unroll
-    for (int k = 0; k < E; ++k) v[k] = __builtin_fmaf(x[k], mul[k % C], nsub[k % C]);
+    for (int k = 0; k < E; ++k)
+      v[k] = normalize<kComp>(x[k], mul[k % C], mul_lo[k % C], nsub[k % C], nsub_lo[k % C]);
     if (P.erase && h >= P.i && h < P.i + P.eh) {
       const int32_t lo = P.j * C - x0, hi = (P.j + P.ew) * C - x0;
 #pragma unroll
@@ -432,12 +466,12 @@ struct ChunkSetup {
 // channels c < C normalized, channels C..3 +0.  A lane's 8 outputs are two
 // whole pixels w0, w0 + 1 (x0 = 4 w0); pixel w takes source pixel W-1-w when
 // flipped, channels in order; an erased pixel is +0 in every channel.
-template <int C>
+template <int C, bool kComp>
 struct Pad4Chunk {
   int32_t x0;
   int32_t w0;
   int32_t direct, mirror;  // source byte of pixel w0, from the row start, unflipped / flipped
-  float mul[C], nsub[C];
+  float mul[C], mul_lo[C], nsub[C], nsub_lo[C];
 
   __device__ __forceinline__ Pad4Chunk(const FusedArgs& a, int32_t first) : x0(first) {
     w0 = first >> 2;
@@ -446,14 +480,18 @@ struct Pad4Chunk {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       mul[c] = a.mul[c];
+      mul_lo[c] = a.mul_lo[c];
       nsub[c] = a.nsub[c];
+      nsub_lo[c] = a.nsub_lo[c];
     }
   }
 
+  template <int kSrc = kSrcAny>
   __device__ __forceinline__ void values(const uint8_t* s_tile, int32_t row_lds,
                                          const SampleParams& P, int32_t h, float (&v)[8]) const {
-    const int32_t b0 = row_lds + (P.flip ? mirror : direct);
-    const int32_t step = P.flip ? -C : C;
+    const bool flip = kSrc != kSrcAny ? kSrc == kSrcFlip : P.flip != 0;
+    const int32_t b0 = row_lds + (flip ? mirror : direct);
+    const int32_t step = flip ? -C : C;
     bool er[2] = {false, false};
     if (P.erase && h >= P.i && h < P.i + P.eh) {
       er[0] = w0 >= P.j && w0 < P.j + P.ew;
@@ -465,7 +503,7 @@ struct Pad4Chunk {
       for (int c = 0; c < 4; ++c) {
         if (c < C) {
           const float x = (float)s_tile[b0 + p * step + c];
-          v[4 * p + c] = er[p] ? 0.0f : __builtin_fmaf(x, mul[c], nsub[c]);
+          v[4 * p + c] = er[p] ? 0.0f : normalize<kComp>(x, mul[c], mul_lo[c], nsub[c], nsub_lo[c]);
         } else {
           v[4 * p + c] = 0.0f;
         }
@@ -556,29 +594,35 @@ __device__ __forceinline__ void load_tile_rows_waves(const FusedArgs& a, const T
 // Work-group size of the tiles kernel: 256 lanes for 8-element (fp16) chunks,
 // 512 for 4-element (fp32) chunks, so that a pass covers whole rows of
 // typical widths with few idle lanes.
+#ifndef FN_TILE_THREADS_F16
+#define FN_TILE_THREADS_F16 256
+#endif
 template <typename OutT>
 constexpr int tiles_threads() {
-  return sizeof(OutT) == 2 ? 256 : 512;
+  return sizeof(OutT) == 2 ? FN_TILE_THREADS_F16 : 512;
 }
 
-// The fused pass, one tile per work-group (grid = total_tiles).  The first
-// ceil(images / 4) wavefronts draw the decisions of the tile's images (a
-// 16-lane group per image) while the other wavefronts DMA the tile into LDS
-// (when every wavefront draws, all of them load afterwards).  After one
-// barrier every lane makes E = 16/sizeof(OutT) consecutive output elements
-// of a row at a time (two whole 4-channel pixels when kPad4) and stores them
-// as one 16-byte vector, lane-contiguous across the wavefront.  Many small
-// independent work-groups per compute unit hide the memory latency.
+// The fused pass, one tile per work-group (grid = total_tiles).  Every
+// wavefront first issues its share of the tile's global-to-LDS DMA loads;
+// then the first ceil(images / 4) wavefronts draw the decisions of the
+// tile's images (a 16-lane group per image) while the loads are in flight.
+// After one barrier every lane makes E = 16/sizeof(OutT) consecutive output
+// elements of a row at a time (two whole 4-channel pixels when kPad4) and
+// stores them as one 16-byte vector, lane-contiguous across the wavefront.
+// A tile of one image reads its decisions into scalar registers and picks
+// the way its source bytes are read (mirrored, aligned dwords or bytes) once.
+// Many small independent work-groups per compute unit hide the memory
+// latency.
 // Requires W*OC a multiple of E (OC = 4 when kPad4, else C) and a 16-byte
 // aligned output; the input may be compact or strided (a.strided).
-template <int C, typename OutT, bool kPad4>
+template <int C, typename OutT, bool kPad4, bool kComp>
 __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(FusedArgs a) {
   constexpr int kThreads = tiles_threads<OutT>();
   constexpr int kWaves = kThreads / 64;
   constexpr int E = 16 / (int)sizeof(OutT);
   constexpr int OC = kPad4 ? 4 : C;  // output channels per pixel
   static_assert(!kPad4 || E == 8, "the padded layout is fp16: two pixels per 16-byte vector");
-  using Setup = typename std::conditional<kPad4, Pad4Chunk<C>, ChunkSetup<C, E>>::type;
+  using Setup = typename std::conditional<kPad4, Pad4Chunk<C, kComp>, ChunkSetup<C, E, kComp>>::type;
   extern __shared__ __align__(16) uint8_t s_lds[];
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
@@ -586,17 +630,16 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   const int n_count = (T.rows - 1) / a.H + 1;
   const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
   const int32_t draw_waves = min(kWaves, (n_count + 3) >> 2);
-  const int32_t load_first = draw_waves < kWaves ? draw_waves : 0;
+  // every wavefront issues its share of the tile's DMA loads first; the
+  // drawing wavefronts then draw while the loads are in flight
+  if (a.strided)
+    load_tile_rows_waves(a, T, s_lds, wave, kWaves);
+  else
+    load_tile_waves(a, T, s_lds, wave, kWaves);
   if (wave < draw_waves) {
     const int slot = (int)(threadIdx.x >> 4);
     const SampleParams p = draw_sample_params16(a.draw, (uint64_t)(T.n_first + slot));
     if ((threadIdx.x & 15u) == 0 && slot < n_count) s_params[slot] = p;
-  }
-  if (wave >= load_first) {
-    if (a.strided)
-      load_tile_rows_waves(a, T, s_lds, wave - load_first, kWaves - load_first);
-    else
-      load_tile_waves(a, T, s_lds, wave - load_first, kWaves - load_first);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wavefront's DMA loads have landed
   __syncthreads();
@@ -622,11 +665,47 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
     if (slot_row < rpi) {
       const Setup cs(a, (ct - slot_row * cpr) * E);
       if (single) {
-        for (int32_t r = slot_row; r < T.rows; r += rpi) {
-          float v[E];
-          cs.values(s_lds, row_lds(r), P0, T.h0 + r, v);
-          store_group<OutT, E, true>(out + (int64_t)r * row_out + cs.x0, v);
-        }
+        // The tile's decisions are the same in every lane: keep them in
+        // scalar registers, and pick the way source bytes are read once per
+        // tile (a scalar branch) instead of per row and lane.
+        SampleParams P;
+        P.flip = __builtin_amdgcn_readfirstlane(P0.flip);
+        P.erase = __builtin_amdgcn_readfirstlane(P0.erase);
+        P.i = __builtin_amdgcn_readfirstlane(P0.i);
+        P.j = __builtin_amdgcn_readfirstlane(P0.j);
+        P.eh = __builtin_amdgcn_readfirstlane(P0.eh);
+        P.ew = __builtin_amdgcn_readfirstlane(P0.ew);
+        auto rows = [&](auto mode) {
+          constexpr int kSrc = decltype(mode)::value;
+          if (a.strided) {
+            for (int32_t r = slot_row; r < T.rows; r += rpi) {
+              float v[E];
+              cs.template values<kSrc>(s_lds, row_lds(r), P, T.h0 + r, v);
+              store_group<OutT, E, true>(out + (int64_t)r * row_out + cs.x0, v);
+            }
+          } else {
+            // compact rows: LDS start and output advance by fixed steps
+            int32_t lds = head + slot_row * row;
+            OutT* dst = out + (int64_t)slot_row * row_out + cs.x0;
+            for (int32_t r = slot_row; r < T.rows; r += rpi) {
+              float v[E];
+              cs.template values<kSrc>(s_lds, lds, P, T.h0 + r, v);
+              store_group<OutT, E, true>(dst, v);
+              lds += rpi * row;
+              dst += (int64_t)rpi * row_out;
+            }
+          }
+        };
+        // compact rows start at head + r * row: all 4-byte aligned when both are
+        const bool aligned = !a.strided && ((head | row) & 3) == 0;
+        if (P.flip)
+          rows(std::integral_constant<int, kSrcFlip>());
+        else if (a.strided)  // each strided row has its own alignment
+          rows(std::integral_constant<int, kSrcAny>());
+        else if (aligned)
+          rows(std::integral_constant<int, kSrcAligned>());
+        else
+          rows(std::integral_constant<int, kSrcBytes>());
       } else {
         for (int32_t r = slot_row; r < T.rows; r += rpi) {
           uint32_t slot;
@@ -685,7 +764,7 @@ __global__ void __launch_bounds__(kBlock) fused_generic_kernel(FusedArgs a) {
     if (!erased && c < C) {
       const int32_t src_w = p.flip ? (W - 1 - w) : w;
       const uint8_t x = a.in[img_base + (int64_t)h * a.in_row_stride + (int64_t)src_w * C + c];
-      v = __builtin_fmaf((float)x, a.mul[c], a.nsub[c]);
+      v = normalize((float)x, a.mul[c], a.mul_lo[c], a.nsub[c], a.nsub_lo[c]);
     }
     out[begin + idx] = to_out<OutT>(v);
   }

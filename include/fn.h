@@ -92,12 +92,18 @@ typedef struct {
  * Result, per sample n with P = fn_params(seed, ...)[n]:
  *   out[n,h,w,c] = +0                                 if P.erase and
  *                                                     P.i <= h < P.i+P.eh and P.j <= w < P.j+P.ew
- *                = x * mul_c - sub_c  (one fma)       otherwise,
- *   x = in[n, h, P.flip ? W-1-w : w, c], mul_c = RN32(1/(255 std_c)),
- *   sub_c = RN32(mean_c/std_c).  The pixel order is mirrored, the channel
- *   order inside a pixel is kept (page sec. 7).  fp16 output is the fp32
- *   value rounded to nearest even.  With FN_OUT_FP16_PAD4, out[n,h,w,c] for
- *   c < C is the fp16 value above and out[n,h,w,c] = +0 for C <= c < 4.
+ *                = (x/255 - mean_c)/std_c             otherwise,
+ *   x = in[n, h, P.flip ? W-1-w : w, c].  The pixel order is mirrored, the
+ *   channel order inside a pixel is kept (page sec. 7).  The value is
+ *   computed as page sec. 7 writes it, x*mul_c - sub_c, with mul_c =
+ *   1/(255 std_c) and sub_c = mean_c/std_c each carried as a pair of fp32
+ *   numbers (their double values split into high and low parts):
+ *   fma(x, mul_hi, -sub_hi) + fma(x, mul_lo, -sub_lo).  fp32 output is within
+ *   2e-6 of the correctly rounded value for |value| < 8 and within about one
+ *   fp32 ulp of it relative to the value; fp16 output is that fp32 value
+ *   rounded to nearest even, within one fp16 ulp of the correctly rounded
+ *   fp32 value.  With FN_OUT_FP16_PAD4, out[n,h,w,c] for c < C is the fp16
+ *   value above and out[n,h,w,c] = +0 for C <= c < 4.
  *
  * Errors: FN_EINVAL for a null pointer (N > 0), a device pointer that is not
  * device memory or whose buffer is shorter than the sizes above, a misaligned

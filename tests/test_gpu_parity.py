@@ -5,12 +5,14 @@ Bars (checked element by element on the same seeded inputs):
     bit-exact;
   - fp32 output: |gpu - oracle| <= 2e-6, erased elements exactly +0.0;
   - fp16 output: |gpu - oracle| <= one fp16 ulp at |oracle|, erased elements
-    exactly +0.  With the MNIST, CIFAR and ImageNet presets every fp16 output
-    also equals the oracle rounded to nearest even (an exhaustive check of
-    all 256 byte values per channel shows the fp32 fma never crosses an fp16
-    rounding midpoint there), so preset workloads assert that exactly; with
-    arbitrary constants the fma's rounding may move 1 ulp, which the bound
-    above allows.
+    exactly +0, for any constants.  The kernels carry 1/(255 std) and
+    mean/std as fp32 high/low pairs, so their fp32 value is within about one
+    fp32 ulp of the oracle's relative to the value itself, also near zero
+    where the value cancels.  With the MNIST, CIFAR and ImageNet presets
+    every fp16 output also equals the oracle rounded to nearest even (an
+    exhaustive check of all 256 byte values per channel shows the kernels'
+    fp32 value never crosses an fp16 rounding midpoint there), so preset
+    workloads assert that exactly.
 """
 from __future__ import annotations
 
@@ -64,10 +66,8 @@ def check_values(got: np.ndarray, ref: np.ndarray, what: str, rne_exact: bool = 
     erased: elements that must be exactly +0; by default the elements where
     the oracle is +0 (no normalized value is exactly 0 at the preset
     constants, so there the two coincide).
-    Bounds: fp32 within FP32_TOL of the oracle (the fma's and constants'
-    roundings); fp16 output is RNE16 of that fp32 value, so within
-    max(1 ulp, FP32_TOL + 1/2 ulp) of the oracle -- the second term only
-    matters within ~0.004 of 0, where a value can cancel exactly."""
+    Bounds: fp32 within FP32_TOL of the oracle; fp16 within one fp16 ulp
+    at |oracle| of the oracle."""
     assert got.shape == ref.shape, what
     zero = ref.view(np.uint32) == 0 if erased is None else np.broadcast_to(erased, ref.shape)
     if got.dtype == np.float32:
@@ -78,7 +78,7 @@ def check_values(got: np.ndarray, ref: np.ndarray, what: str, rne_exact: bool = 
     assert got.dtype == np.float16
     err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
     u = ulp16(ref)
-    bad = err > np.maximum(u, FP32_TOL + 0.5 * u)
+    bad = err > u
     assert not np.any(bad), (what, int(bad.sum()), float(err.max()))
     assert np.all(got.view(np.uint16)[zero] == 0), what
     same = float(np.mean(got.view(np.uint16) == ref.astype(np.float16).view(np.uint16)))
@@ -143,8 +143,10 @@ def test_fused_full_batch(b, name):
 
 def test_stress_eight_back_to_back_launches(b):
     """2048 images, eight launches on one stream with seeds 123..130 into
-    eight distinct outputs; every launch's decisions are checked in full,
-    and a sample of images per launch element by element."""
+    eight distinct outputs; every launch's decisions and every output
+    element are checked, launch by launch in chunks of 256 images to bound
+    host memory.  The ImageNet preset makes every fp16 output equal to the
+    oracle rounded to nearest even, erased elements included (+0)."""
     w = synth.WORKLOADS["stress"]
     x = w.make_input()
     xt = torch.from_numpy(x).cuda()
@@ -154,20 +156,23 @@ def test_stress_eight_back_to_back_launches(b):
     for seed, out in zip(w.seeds, outs):
         run_fused(b, xt, w.N, w.H, w.W, w.C, wl_dict(w), seed, w.out_dtype, out)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(99)
+    chunk = 256
     for seed, out in zip(w.seeds, outs):
         P = oracle.params(seed, 0, w.N, w.H, w.W, w.flip_p, w.erase_p, w.scale, w.ratio)
         got_p = gpu_params(b, w, seed)
         assert got_p.tobytes() == P.tobytes(), seed
-        picks = sorted({0, 1, w.N - 1, *rng.choice(w.N, 9, replace=False).tolist()})
-        idx = torch.tensor(picks, device="cuda")
-        got = out.index_select(0, idx).cpu().numpy()
-        for k, n in enumerate(picks):
-            ref, _ = oracle.fused_normalize(x[n:n + 1], w.mean, w.std, w.flip_p, w.erase_p,
-                                            w.scale, w.ratio, seed=seed, first_n=n)
-            check_values(got[k:k + 1], ref, f"stress seed={seed} n={n}")
+        for c0 in range(0, w.N, chunk):
+            c1 = min(w.N, c0 + chunk)
+            ref, _ = oracle.fused_normalize(x[c0:c1], w.mean, w.std, w.flip_p, w.erase_p,
+                                            w.scale, w.ratio, seed=seed, first_n=c0,
+                                            threads=THREADS)
+            got = out[c0:c1].cpu().numpy()
+            if not np.array_equal(got.view(np.uint16), ref.astype(np.float16).view(np.uint16)):
+                check_values(got, ref, f"stress seed={seed} images {c0}..{c1 - 1}")
+                raise AssertionError(f"stress seed={seed} images {c0}..{c1 - 1}: not RNE16(oracle)")
         say(f"  seed {seed}: {int(P['flip'].sum())} flipped, {int(P['erase'].sum())} erased, "
-            f"sampled {picks}")
+            f"all {w.N} images equal RNE16(oracle)")
+        del out
 
 
 EDGE_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1, 3),
