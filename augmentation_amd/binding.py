@@ -45,6 +45,7 @@ _SIGS = {
     "fn_test_erase_dims": [_P, _P, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _P, _P, _P, _P],
     "fn_test_cr_ops": [_i32, _P, _P, _i64, _P, _P],
     "fn_test_copy": [_P, _P, _i64, _P],
+    "fn_test_stream": [_P, _P, _i64, _i32, _P],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -53,7 +54,8 @@ _lib.fn_last_error.argtypes = []
 _lib.fn_last_error.restype = ctypes.c_char_p
 
 EXPORTED = ("fn_fused_normalize", "fn_fused_normalize_ex", "fn_params", "fn_params_ex",
-            "fn_last_error", "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_copy")
+            "fn_last_error", "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_copy",
+            "fn_test_stream")
 
 
 class FnError(RuntimeError):
@@ -143,6 +145,10 @@ def fn_test_cr_ops(op, a, b, count, out, stream=None) -> int:
 
 def fn_test_copy(src, dst, nbytes, stream=None) -> int:
     return _check(_lib.fn_test_copy(_addr(src), _addr(dst), nbytes, _stream(stream)))
+
+
+def fn_test_stream(src, dst, in_bytes, widen, stream=None) -> int:
+    return _check(_lib.fn_test_stream(_addr(src), _addr(dst), in_bytes, widen, _stream(stream)))
 
 
 # ------------------------------------------------------------ tensor helpers

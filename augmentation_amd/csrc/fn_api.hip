@@ -38,10 +38,25 @@ int ok() {
 
 bool in_unit(float p) { return p >= 0.0f && p <= 1.0f; }  // false for NaN
 
+// The calling thread's current device.
+int current_device(int* dev) {
+  if (hipGetDevice(dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FN_EHIP, "hipGetDevice failed");
+  }
+  return FN_OK;
+}
+
 // The buffer [p, p + bytes) must be device memory of the current device,
-// inside one allocation.  Failed queries leave no sticky HIP error behind.
-int check_device_range(const void* p, size_t bytes, const char* name) {
+// inside one allocation.  *dev caches the current device across the checks
+// of one call (-1: not queried yet).  Failed queries leave no sticky HIP
+// error behind.
+int check_device_range(const void* p, size_t bytes, const char* name, int* dev) {
   if (p == nullptr) return fail(FN_EINVAL, "%s is NULL", name);
+  if (*dev < 0) {
+    const int rc = current_device(dev);
+    if (rc) return rc;
+  }
   hipPointerAttribute_t attr;
   hipError_t e = hipPointerGetAttributes(&attr, p);
   if (e != hipSuccess) {
@@ -50,14 +65,9 @@ int check_device_range(const void* p, size_t bytes, const char* name) {
   }
   if (attr.type != hipMemoryTypeDevice)
     return fail(FN_EINVAL, "%s is not device memory (memory type %d)", name, (int)attr.type);
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(FN_EHIP, "hipGetDevice failed");
-  }
-  if (attr.device != dev)
+  if (attr.device != *dev)
     return fail(FN_EINVAL, "%s lives on device %d, the current device is %d", name, attr.device,
-                dev);
+                *dev);
   hipDeviceptr_t base = nullptr;
   size_t size = 0;
   e = hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p);
@@ -111,14 +121,9 @@ unsigned blocks_for(int64_t items, int64_t per_block) {
   return (unsigned)((items + per_block - 1) / per_block);
 }
 
-// Compute units of the current device, queried once per device.
-int device_cu_count(int* cus) {
+// Compute units of device `dev`, queried once per device.
+int device_cu_count(int dev, int* cus) {
   static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(FN_EHIP, "hipGetDevice failed");
-  }
   if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed) > 0) {
     *cus = cache[dev].load(std::memory_order_relaxed);
     return FN_OK;
@@ -134,15 +139,10 @@ int device_cu_count(int* cus) {
   return FN_OK;
 }
 
-// LDS bytes per compute unit of the current device, cached per device; 0 if
-// the runtime does not report it.
-size_t device_lds_per_cu() {
+// LDS bytes per compute unit of device `dev`, cached per device; 0 if the
+// runtime does not report it.
+size_t device_lds_per_cu(int dev) {
   static std::atomic<long> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
   if (dev >= 0 && dev < 64) {
     const long c = cache[dev].load(std::memory_order_relaxed);
     if (c != 0) return c > 0 ? (size_t)c : 0;
@@ -161,9 +161,9 @@ size_t device_lds_per_cu() {
 // that at most kWgsPerCu work-groups fit on a compute unit (fewer resident
 // work-groups queue less at the memory and finish sooner; measured).  The
 // padding never exceeds the 64 KB a work-group may request.
-size_t tiles_lds_bytes(int32_t buffer_bytes) {
+size_t tiles_lds_bytes(int dev, int32_t buffer_bytes) {
   size_t lds = (size_t)buffer_bytes;
-  const size_t per_cu = device_lds_per_cu();
+  const size_t per_cu = device_lds_per_cu(dev);
   if (fn::kWgsPerCu > 0 && per_cu > 0) {
     const size_t cap = per_cu / fn::kWgsPerCu;   // kWgsPerCu fit ...
     const size_t over = per_cu / (fn::kWgsPerCu + 1) + 1;  // ... one more does not
@@ -280,7 +280,7 @@ uint32_t float_bits(float v) {
 // byte value x of every channel: the fp32 bits, or the binary16 bits of
 // their rounding.  The inputs are bytes, so this covers every element the
 // kernel can meet.
-bool single_fma_exact(const fn::FusedArgs& a, int C, int out_dtype) {
+bool single_fma_exact_uncached(const fn::FusedArgs& a, int C, int out_dtype) {
   for (int c = 0; c < C; ++c) {
     for (int x = 0; x < 256; ++x) {
       const float xf = (float)x;
@@ -296,6 +296,33 @@ bool single_fma_exact(const fn::FusedArgs& a, int C, int out_dtype) {
   return true;
 }
 
+// single_fma_exact_uncached, remembered per thread for the last constants
+// (a training loop calls with the same mean and std every time).
+bool single_fma_exact(const fn::FusedArgs& a, int C, int out_dtype) {
+  struct Last {
+    bool valid = false, result = false;
+    int C = 0, out_dtype = 0;
+    float mul[4], mul_lo[4], nsub[4], nsub_lo[4];
+  };
+  thread_local Last last;
+  const bool same = last.valid && last.C == C && last.out_dtype == out_dtype &&
+                    std::memcmp(last.mul, a.mul, sizeof(last.mul)) == 0 &&
+                    std::memcmp(last.mul_lo, a.mul_lo, sizeof(last.mul_lo)) == 0 &&
+                    std::memcmp(last.nsub, a.nsub, sizeof(last.nsub)) == 0 &&
+                    std::memcmp(last.nsub_lo, a.nsub_lo, sizeof(last.nsub_lo)) == 0;
+  if (!same) {
+    last.result = single_fma_exact_uncached(a, C, out_dtype);
+    last.C = C;
+    last.out_dtype = out_dtype;
+    std::memcpy(last.mul, a.mul, sizeof(last.mul));
+    std::memcpy(last.mul_lo, a.mul_lo, sizeof(last.mul_lo));
+    std::memcpy(last.nsub, a.nsub, sizeof(last.nsub));
+    std::memcpy(last.nsub_lo, a.nsub_lo, sizeof(last.nsub_lo));
+    last.valid = true;
+  }
+  return last.result;
+}
+
 // Tile plan of the tiles kernel: the largest tile of at most kTileBytesTarget
 // input bytes (whole rows, or whole images when one fits), shrunk -- down to
 // kMinTileBytes -- so that the batch gives every compute unit at least 8
@@ -303,21 +330,24 @@ bool single_fma_exact(const fn::FusedArgs& a, int C, int out_dtype) {
 // Sets the tile fields of `a`.
 int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elems, int cus,
                int64_t row_slot) {
+  // LDS bytes one row occupies: the row itself, or its slot of whole
+  // granules when strided (never fewer than 32 bytes, however narrow the row)
+  const int64_t row_lds = row_slot > 0 ? row_slot : row;
   int64_t target = fn::kTileBytesTarget;
   const int64_t want = (int64_t)cus * 8;
   if (elems / want < target) target = std::max<int64_t>(elems / want, fn::kMinTileBytes);
-  if (target < row) target = row;
-  const int64_t image_bytes = (int64_t)H * row;
+  if (target < row_lds) target = row_lds;
+  const int64_t image_lds = (int64_t)H * row_lds;
   int64_t tile_bytes;
-  if (image_bytes <= target) {
-    const int64_t g = std::min<int64_t>(target / image_bytes, fn::kMaxImagesPerBlock);
+  if (image_lds <= target) {
+    const int64_t g = std::min<int64_t>(target / image_lds, fn::kMaxImagesPerBlock);
     a->images_per_tile = (int32_t)g;
     a->rows_per_tile = H;
     a->tiles_per_image = 1;
     a->total_tiles = (N + g - 1) / g;
-    tile_bytes = g * image_bytes;
+    tile_bytes = g * H * row;
   } else {
-    const int64_t r = std::max<int64_t>(1, std::min<int64_t>(H, target / row));
+    const int64_t r = std::max<int64_t>(1, std::min<int64_t>(H, target / row_lds));
     a->images_per_tile = 1;
     a->rows_per_tile = (int32_t)r;
     a->tiles_per_image = (int32_t)((H + r - 1) / r);
@@ -362,7 +392,8 @@ FN_EXPORT int fn_params_ex(uint64_t seed, int64_t first_sample_id, int64_t N, in
   if (N < 0) return fail(FN_EINVAL, "N must be >= 0");
   if (N > ((int64_t)1 << 36)) return fail(FN_EOVERFLOW, "N too large");
   if (N == 0) return ok();
-  rc = check_device_range(params_dev, (size_t)N * sizeof(fn_sample_params), "params_dev");
+  int dev = -1;
+  rc = check_device_range(params_dev, (size_t)N * sizeof(fn_sample_params), "params_dev", &dev);
   if (rc) return rc;
   const int64_t samples_per_block = fn::kBlock / 16;
   fn::params_kernel<<<blocks_for(N, samples_per_block), fn::kBlock, 0, (hipStream_t)stream>>>(
@@ -437,9 +468,10 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
 
   if ((uintptr_t)out_dev % (uintptr_t)out_bytes != 0)
     return fail(FN_EINVAL, "out_dev must be aligned to its element size (%d bytes)", out_bytes);
-  rc = check_device_range(in_u8_dev, (size_t)span, "in_u8_dev");
+  int dev = -1;
+  rc = check_device_range(in_u8_dev, (size_t)span, "in_u8_dev", &dev);
   if (rc) return rc;
-  rc = check_device_range(out_dev, (size_t)out_elems * out_bytes, "out_dev");
+  rc = check_device_range(out_dev, (size_t)out_elems * out_bytes, "out_dev", &dev);
   if (rc) return rc;
   const uintptr_t i0 = (uintptr_t)in_u8_dev, i1 = i0 + (uintptr_t)span;
   const uintptr_t o0 = (uintptr_t)out_dev, o1 = o0 + (uintptr_t)out_elems * out_bytes;
@@ -475,7 +507,7 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
   if ((uintptr_t)out_dev % 16 == 0 && row_out % (16 / out_bytes) == 0 &&
       row <= fn::kTileBytesMax) {
     int cus = 0;
-    rc = device_cu_count(&cus);
+    rc = device_cu_count(dev, &cus);
     if (rc) return rc;
     // strided rows: one slot of whole 16-byte granules per row
     const int64_t row_slot = strided ? (15 + row + 15) / 16 * 16 : 0;
@@ -489,7 +521,7 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
     a.div_tpi = make_fast_div((uint32_t)a.tiles_per_image);
     const bool comp = !single_fma_exact(a, C, out_dtype);
     launch_tiles(a, C, out_dtype, comp, (unsigned)a.total_tiles,
-                 tiles_lds_bytes(a.lds_buffer_bytes), st);
+                 tiles_lds_bytes(dev, a.lds_buffer_bytes), st);
     return launch_status("fused_tiles_kernel launch");
   }
   const int px = out_dtype == FN_OUT_FP16_PAD4 || strided
@@ -560,11 +592,12 @@ FN_EXPORT int fn_test_erase_dims(const uint32_t* w_scale_dev, const uint32_t* w_
   if (count < 0) return fail(FN_EINVAL, "count must be >= 0");
   if (count > ((int64_t)1 << 36)) return fail(FN_EOVERFLOW, "count too large");
   if (count == 0) return ok();
-  if ((rc = check_device_range(w_scale_dev, count * 4, "w_scale_dev")) ||
-      (rc = check_device_range(w_ratio_dev, count * 4, "w_ratio_dev")) ||
-      (rc = check_device_range(eh_dev, count * 4, "eh_dev")) ||
-      (rc = check_device_range(ew_dev, count * 4, "ew_dev")) ||
-      (rc = check_device_range(accepted_dev, count, "accepted_dev")))
+  int dev = -1;
+  if ((rc = check_device_range(w_scale_dev, count * 4, "w_scale_dev", &dev)) ||
+      (rc = check_device_range(w_ratio_dev, count * 4, "w_ratio_dev", &dev)) ||
+      (rc = check_device_range(eh_dev, count * 4, "eh_dev", &dev)) ||
+      (rc = check_device_range(ew_dev, count * 4, "ew_dev", &dev)) ||
+      (rc = check_device_range(accepted_dev, count, "accepted_dev", &dev)))
     return rc;
   fn::erase_dims_kernel<<<blocks_for(count, fn::kBlock), fn::kBlock, 0, (hipStream_t)stream>>>(
       a, w_scale_dev, w_ratio_dev, count, eh_dev, ew_dev, accepted_dev);
@@ -578,10 +611,11 @@ FN_EXPORT int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev,
   if (count > ((int64_t)1 << 36)) return fail(FN_EOVERFLOW, "count too large");
   if (count == 0) return ok();
   int rc;
-  if ((rc = check_device_range(a_dev, count * 4, "a_dev")) ||
-      (rc = check_device_range(out_dev, count * 4, "out_dev")))
+  int dev = -1;
+  if ((rc = check_device_range(a_dev, count * 4, "a_dev", &dev)) ||
+      (rc = check_device_range(out_dev, count * 4, "out_dev", &dev)))
     return rc;
-  if (op == 2 && (rc = check_device_range(b_dev, count * 4, "b_dev"))) return rc;
+  if (op == 2 && (rc = check_device_range(b_dev, count * 4, "b_dev", &dev))) return rc;
   fn::cr_ops_kernel<<<blocks_for(count, fn::kBlock), fn::kBlock, 0, (hipStream_t)stream>>>(
       op, a_dev, op == 2 ? b_dev : a_dev, count, out_dev);
   return launch_status("cr_ops_kernel launch");
@@ -593,8 +627,9 @@ FN_EXPORT int fn_test_copy(const void* src_dev, void* dst_dev, int64_t bytes, vo
     return fail(FN_EINVAL, "pointers must be 16-byte aligned");
   if (bytes == 0) return ok();
   int rc;
-  if ((rc = check_device_range(src_dev, (size_t)bytes, "src_dev")) ||
-      (rc = check_device_range(dst_dev, (size_t)bytes, "dst_dev")))
+  int dev = -1;
+  if ((rc = check_device_range(src_dev, (size_t)bytes, "src_dev", &dev)) ||
+      (rc = check_device_range(dst_dev, (size_t)bytes, "dst_dev", &dev)))
     return rc;
   const uintptr_t s0 = (uintptr_t)src_dev, d0 = (uintptr_t)dst_dev;
   if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes)
@@ -605,4 +640,34 @@ FN_EXPORT int fn_test_copy(const void* src_dev, void* dst_dev, int64_t bytes, vo
   fn::copy_kernel<<<(unsigned)blocks, fn::kBlock, 0, (hipStream_t)stream>>>(
       reinterpret_cast<const uint4*>(src_dev), reinterpret_cast<uint4*>(dst_dev), vecs);
   return launch_status("copy_kernel launch");
+}
+
+FN_EXPORT int fn_test_stream(const void* src_dev, void* dst_dev, int64_t in_bytes, int32_t widen,
+                             void* stream) {
+  if (widen != 2 && widen != 4) return fail(FN_EINVAL, "widen must be 2 or 4");
+  const int64_t per_lane = 16 / widen;  // input bytes per lane
+  if (in_bytes < 0 || in_bytes % per_lane != 0)
+    return fail(FN_EINVAL, "in_bytes must be a multiple of %d", (int)per_lane);
+  if (((uintptr_t)src_dev % (uintptr_t)per_lane) != 0 || ((uintptr_t)dst_dev & 15u) != 0)
+    return fail(FN_EINVAL, "src_dev must be %d-byte aligned and dst_dev 16-byte aligned",
+                (int)per_lane);
+  if (in_bytes > ((int64_t)1 << 40)) return fail(FN_EOVERFLOW, "in_bytes too large");
+  if (in_bytes == 0) return ok();
+  int rc;
+  int dev = -1;
+  if ((rc = check_device_range(src_dev, (size_t)in_bytes, "src_dev", &dev)) ||
+      (rc = check_device_range(dst_dev, (size_t)(in_bytes * widen), "dst_dev", &dev)))
+    return rc;
+  const uintptr_t s0 = (uintptr_t)src_dev, d0 = (uintptr_t)dst_dev;
+  if (s0 < d0 + (uintptr_t)(in_bytes * widen) && d0 < s0 + (uintptr_t)in_bytes)
+    return fail(FN_EINVAL, "source and destination overlap");
+  const int64_t lanes = in_bytes / per_lane;
+  const unsigned grid = blocks_for(lanes, fn::kBlock);
+  if (widen == 2)
+    fn::stream_kernel<2><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(
+        reinterpret_cast<const uint8_t*>(src_dev), reinterpret_cast<fn::u32x4*>(dst_dev), lanes);
+  else
+    fn::stream_kernel<4><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(
+        reinterpret_cast<const uint8_t*>(src_dev), reinterpret_cast<fn::u32x4*>(dst_dev), lanes);
+  return launch_status("stream_kernel launch");
 }

@@ -22,6 +22,7 @@
 //   normalize()), stored as fp32 or round-to-nearest-even fp16.
 //   erase_dims_kernel,
 //   cr_ops_kernel,
+//   stream_kernel,
 //   copy_kernel            test and measurement hooks.
 #pragma once
 
@@ -64,6 +65,7 @@ namespace fn {
 #ifndef FN_WGS_PER_CU
 #define FN_WGS_PER_CU 6
 #endif
+
 
 constexpr int kBlock = 256;             // four wave64 wavefronts
 constexpr int kTileBytesTarget = FN_TILE_BYTES;
@@ -799,6 +801,30 @@ __global__ void __launch_bounds__(kBlock) cr_ops_kernel(int32_t op, const float*
     r = cr_divf(x[s], y[s]);
   }
   out[s] = r;
+}
+
+// The operation's traffic without its arithmetic: every lane reads 16/K
+// bytes and writes them widened to K bytes each (zero-extended) as one
+// 16-byte streaming store, lane-contiguous; K = 2 is the fp16 operation's
+// 1:2 read:write mix, K = 4 the fp32 one's 1:4.  One lane per 16 output
+// bytes, one-shot grid: the shape that moved these mixes fastest on the
+// hardware, so its rate is the practical roof for the fused kernel.
+template <int K>
+__global__ void __launch_bounds__(kBlock) stream_kernel(const uint8_t* __restrict__ src,
+                                                        u32x4* __restrict__ dst, int64_t lanes) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= lanes) return;
+  u32x4 q;
+  if constexpr (K == 2) {
+    const uint2 w = reinterpret_cast<const uint2*>(src)[i];
+    // v_perm_b32 byte selectors: 0..3 pick bytes of the second operand, 12 gives 0
+    q = u32x4{__builtin_amdgcn_perm(0u, w.x, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.x, 0x0C030C02u),
+              __builtin_amdgcn_perm(0u, w.y, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.y, 0x0C030C02u)};
+  } else {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(src)[i];
+    q = u32x4{w & 0xFFu, (w >> 8) & 0xFFu, (w >> 16) & 0xFFu, w >> 24};
+  }
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(dst + i), "v"(q) : "memory");
 }
 
 __global__ void __launch_bounds__(kBlock) copy_kernel(const uint4* __restrict__ src,

@@ -24,9 +24,13 @@ Timing: about --prewarm-seconds of untimed launches (the GPU clocks down
 while the host builds inputs), --warmup untimed launches, then --steps timed
 launches between two device synchronisations.
 
-Extra legs: a plain 16-byte copy kernel moving the same byte count gives
-the practical bandwidth ceiling; --all adds one line per workload on
-stderr.
+Extra legs: stream_ceiling times the library's streaming reference
+(fn_test_stream: the same read:write mix and byte count with no arithmetic,
+one 16-byte streaming store per lane), the practical roof for the fused
+kernel; host_us is the host time per call while the timed launches are
+enqueued; --all adds one line per workload on stderr; --sweep instead prints
+per-batch-size lines for the headline shape (the fused call, the streaming
+reference, and a minimal launch) and a fit of time = fixed + per-image cost.
 """
 from __future__ import annotations
 
@@ -112,12 +116,14 @@ def host_threads() -> int:
     return max(1, min(n, 16))  # the machine's CPU share for one GPU
 
 
-def time_launches(launch, steps: int, warmup: int, sets: int, stream, prewarm_s: float) -> float:
+def time_launches(launch, steps: int, warmup: int, sets: int, stream, prewarm_s: float,
+                  host: list | None = None) -> float:
     """Average milliseconds per launch over `steps` launches (events on the
     launch stream), after `warmup` untimed ones.  Before those, launches run
     untimed for about `prewarm_s` seconds: the GPU clocks down while the host
     prepares inputs, and a few warmup launches (well under a millisecond)
-    do not bring it back up."""
+    do not bring it back up.  `host`, if given, receives the host time per
+    call (ms) spent enqueuing the timed launches."""
     import torch
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < prewarm_s:
@@ -130,10 +136,14 @@ def time_launches(launch, steps: int, warmup: int, sets: int, stream, prewarm_s:
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
+    h0 = time.perf_counter()
     for k in range(steps):
         launch(k % sets)
+    h1 = time.perf_counter()
     end.record(stream)
     torch.cuda.synchronize()
+    if host is not None:
+        host.append((h1 - h0) / steps * 1e3)
     return start.elapsed_time(end) / steps
 
 
@@ -177,31 +187,91 @@ def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -
                                     w.scale[0], w.scale[1], w.ratio[0], w.ratio[1],
                                     seeds[k % len(seeds)], 0, w.out_dtype, outs[k], stream)
 
-    ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s)
+    host = []
+    ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s, host)
     med = median_call_ms(launch, min(steps, 200), sets, stream)
     del ins, outs
     torch.cuda.empty_cache()
-    return {"ms": ms, "median_call_ms": med, "images_per_s": w.N / (ms * 1e-3),
+    return {"ms": ms, "median_call_ms": med, "host_ms": host[0], "images_per_s": w.N / (ms * 1e-3),
             "gbs": w.nominal_bytes / (ms * 1e-3) / 1e9}
 
 
-def bench_copy(b, nbytes: int, steps: int, warmup: int, sets: int, prewarm_s: float) -> dict:
-    """The plain copy kernel moving nbytes per launch (nbytes/2 read, nbytes/2 written)."""
+def stream_widen(w) -> int:
+    """Bytes written per byte read by the streaming reference for workload
+    w: 2 for fp16 outputs, 4 for fp32."""
+    return 4 if w.out_dtype == 0 else 2
+
+
+def bench_stream(b, nbytes: int, widen: int, steps: int, warmup: int, sets: int,
+                 prewarm_s: float) -> dict:
+    """The streaming reference moving about nbytes per launch: nbytes/(1+widen)
+    read, widen times that written."""
     import torch
     stream = torch.cuda.current_stream()
-    half = (nbytes // 2) // 16 * 16
-    src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(sets)]
-    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(sets)]
-    for s in src:
-        s.fill_(1)
+    inb = (nbytes // (1 + widen)) // 16 * 16
+    src = [torch.ones(inb, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    dst = [torch.empty(inb * widen, dtype=torch.uint8, device="cuda") for _ in range(sets)]
 
     def launch(k):
-        b.fn_test_copy(src[k], dst[k], half, stream)
+        b.fn_test_stream(src[k], dst[k], inb, widen, stream)
 
     ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s)
     del src, dst
     torch.cuda.empty_cache()
-    return {"ms": ms, "gbs": 2 * half / (ms * 1e-3) / 1e9, "bytes": 2 * half}
+    moved = inb * (1 + widen)
+    return {"ms": ms, "gbs": moved / (ms * 1e-3) / 1e9, "bytes": moved}
+
+
+def sweep(b, steps: int, warmup: int, prewarm_s: float, sizes) -> None:
+    """Per-launch time against batch size on the headline shape: the fused
+    call, the streaming reference with the same bytes, and the streaming
+    reference on 16 bytes (the cost of a launch itself).  Fits
+    t(N) = fixed + N * per_image over the sizes; one JSON line each."""
+    import numpy as np
+    import torch
+    from augmentation_amd import synth
+    stream = torch.cuda.current_stream()
+    w = synth.WORKLOADS[synth.HEADLINE]
+    img = w.H * w.W * w.C
+    tiny_src = torch.ones(16, dtype=torch.uint8, device="cuda")
+    tiny_dst = torch.empty(32, dtype=torch.uint8, device="cuda")
+    floor = time_launches(lambda k: b.fn_test_stream(tiny_src, tiny_dst, 8, 2, stream),
+                          max(steps, 1000), warmup, 1, stream, prewarm_s)
+    print(json.dumps({"sweep": "launch_floor", "us": round(floor * 1e3, 3),
+                      "what": "fn_test_stream on 8 bytes, back to back"}), flush=True)
+    base = torch.from_numpy(w.make_input()).cuda()
+    pts = {"fused": [], "stream": []}
+    for N in sizes:
+        sets = max(2, -(-1_200_000_000 // (3 * N * img)))
+        reps = -(-N // w.N)
+        xs = base.repeat(reps, 1, 1, 1)[:N].contiguous()
+        ins = [xs] + [xs.clone() for _ in range(sets - 1)]
+        outs = [torch.empty((N, w.H, w.W, w.C), dtype=torch.float16, device="cuda")
+                for _ in range(sets)]
+
+        def fused(k):
+            b.fn_fused_normalize(ins[k], N, w.H, w.W, w.C, w.mean, w.std, w.flip_p, w.erase_p,
+                                 w.scale[0], w.scale[1], w.ratio[0], w.ratio[1], w.seeds[0],
+                                 w.out_dtype, outs[k], stream)
+
+        def ref(k):
+            b.fn_test_stream(ins[k], outs[k], N * img, 2, stream)
+
+        n_steps = steps if N <= 512 else max(20, steps // 5)
+        for name, fn in (("fused", fused), ("stream", ref)):
+            ms = time_launches(fn, n_steps, warmup, sets, stream, prewarm_s)
+            pts[name].append((N, ms * 1e3))
+            print(json.dumps({"sweep": name, "N": N, "us": round(ms * 1e3, 3),
+                              "tbs": round(3 * N * img / (ms * 1e-3) / 1e12, 3)}), flush=True)
+        del ins, outs, xs
+        torch.cuda.empty_cache()
+    for name, p in pts.items():
+        n = np.array([q[0] for q in p], float)
+        t = np.array([q[1] for q in p])
+        per, fixed = np.polyfit(n, t, 1)
+        print(json.dumps({"sweep": "fit", "kernel": name, "fixed_us": round(fixed, 3),
+                          "per_image_ns": round(per * 1e3, 2),
+                          "streaming_tbs": round(3 * img / (per * 1e-6) / 1e12, 3)}), flush=True)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -246,7 +316,10 @@ def main() -> int:
                     help="untimed launches before the warmup ones")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-copy", action="store_true")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming reference")
+    ap.add_argument("--sweep", default=None, metavar="N,N,...",
+                    help="time the headline shape at these batch sizes (and the streaming "
+                         "reference and a minimal launch) instead of the JSON line")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--workload", default=None,
                     help="time this workload instead of the headline one (the JSON line then "
@@ -266,6 +339,10 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(b, args.steps, args.warmup, args.prewarm_seconds,
+              [int(v) for v in args.sweep.split(",")])
+        return 0
     name = args.workload or synth.HEADLINE
     if name not in synth.WORKLOADS:
         print(f"unknown workload {name!r}; known: {', '.join(synth.WORKLOADS)}", file=sys.stderr)
@@ -299,12 +376,14 @@ def main() -> int:
                                      if traffic else None),
                      "bytes_per_launch": w.nominal_bytes},
         "median_call_ms": round(r["median_call_ms"], 5),
+        "host_ms": round(r["host_ms"], 5),
     }
-    if not args.no_copy:
-        c = bench_copy(b, w.nominal_bytes, args.steps, args.warmup, args.sets, args.prewarm_seconds)
-        line["copy_ceiling"] = {"gbs": round(c["gbs"], 1), "bytes_per_launch": c["bytes"],
-                                "ms": round(c["ms"], 5),
-                                "fused_vs_copy": round(achieved / c["gbs"], 4)}
+    if not args.no_stream:
+        c = bench_stream(b, w.nominal_bytes, stream_widen(w), args.steps, args.warmup, args.sets,
+                         args.prewarm_seconds)
+        line["stream_ceiling"] = {"gbs": round(c["gbs"], 1), "bytes_per_launch": c["bytes"],
+                                  "ms": round(c["ms"], 5),
+                                  "fused_vs_stream": round(achieved / c["gbs"], 4)}
     if args.all:
         for name, wl in synth.WORKLOADS.items():
             rr = bench_workload(b, wl, max(10, args.steps // 4), 5, args.sets if wl.N < 1024 else 2,

@@ -222,6 +222,16 @@ int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev, int64_t c
  * and for calibrating hardware byte counters. */
 int fn_test_copy(const void* src_dev, void* dst_dev, int64_t bytes, void* stream);
 
+/* The operation's traffic without its arithmetic, as the practical bandwidth
+ * roof of the fused kernels: reads in_bytes from src_dev and writes each byte
+ * zero-extended to `widen` bytes (2: the fp16 operation's 1:2 read:write mix,
+ * 4: the fp32 one's 1:4), in_bytes * widen bytes in all, as 16-byte streaming
+ * stores.  in_bytes a multiple of 16/widen; src_dev aligned to 16/widen
+ * bytes, dst_dev to 16; no overlap.  Errors as above (FN_EINVAL for any other
+ * widen). */
+int fn_test_stream(const void* src_dev, void* dst_dev, int64_t in_bytes, int32_t widen,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,10 @@ WINDOWS = [
     (3, 20, 21, 4, 17, 20, 2, 1, 0, 1),            # four channels
     (2, 9, 1100, 3, 7, 1024, 1, 37, 9, 3),         # rows wider than a pass of the lanes
     (3, 12, 14, 2, 12, 13, 0, 1, 1, 0),            # odd width
+    # narrow rows of many tall images: each row takes a 32-byte LDS slot, so
+    # tiles are sized by slots, not by row bytes
+    (1024, 4100, 8, 1, 4096, 4, 2, 3, 0, 0),
+    (2048, 1030, 12, 1, 1024, 8, 3, 2, 0, 0),
 ]
 
 
@@ -63,11 +67,9 @@ def run_window(b, case, out_dtype, out_aligned, first_sample_id=0, image_stride_
     buf[base_off:] = torch.from_numpy(flat).cuda()
     first = base_off + y0 * row_stride + x0 * C
     # the window, copied out compactly: what the oracle reads
-    x = np.empty((N, H, W, C), dtype=np.uint8)
-    for n in range(N):
-        for h in range(H):
-            o = n * image_stride + (y0 + h) * row_stride + x0 * C
-            x[n, h] = flat[o:o + W * C].reshape(W, C)
+    x = np.lib.stride_tricks.as_strided(flat[y0 * row_stride + x0 * C:], shape=(N, H, W * C),
+                                        strides=(image_stride, row_stride, 1))
+    x = np.ascontiguousarray(x).reshape(N, H, W, C)
     oc = 4 if out_dtype == 2 else C
     esz = 4 if out_dtype == 0 else 2
     out_off = 4096 if out_aligned else 4096 + esz

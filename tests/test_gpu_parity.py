@@ -347,6 +347,48 @@ def test_bad_pointers_rejected_without_launch(b):
     assert float(y) == x.numel()
 
 
+@pytest.mark.parametrize("widen", [2, 4])
+def test_stream_hook(b, widen):
+    """fn_test_stream writes every input byte zero-extended to `widen` bytes."""
+    n = (1 << 20) + 16 * 37
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.full((n * widen,), 0xA5, dtype=torch.uint8, device="cuda")
+    b.fn_test_stream(src, dst, n, widen)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint16 if widen == 2 else np.uint32)
+    np.testing.assert_array_equal(got, src.cpu().numpy().astype(got.dtype))
+
+
+# Constants whose single-fma result is not always the correctly rounded one:
+# mean 0.4 puts x = 102 within 3e-8 of an exact cancellation, where one fma on
+# rounded constants errs by several fp16 ulps of the tiny result.
+CANCELLING = [((0.4, 0.4, 0.4), (0.2, 0.2, 0.2)), ((0.6, 0.2, 0.8), (0.3, 0.7, 0.05)),
+              ((1.0, 0.0, 0.5), (1.0, 1.0, 0.5))]
+
+
+@pytest.mark.parametrize("consts", CANCELLING)
+@pytest.mark.parametrize("out_dtype", [0, 1, 2])
+def test_tiles_kernel_with_cancelling_constants(b, consts, out_dtype):
+    """The tiles kernel (16-byte aligned output, whole 16-byte vectors per
+    row) with constants where values cancel to (near) zero: fp32 within 2e-6,
+    fp16 within one fp16 ulp of the oracle, for every byte value."""
+    mean, std = consts
+    N, H, W, C = 6, 40, 48, 3
+    x = np.tile(np.arange(256, dtype=np.uint8), N * H * W * C // 256 + 1)[:N * H * W * C]
+    x = np.random.default_rng(3).permutation(x).reshape(N, H, W, C)
+    say(f"cancelling constants {consts} out_dtype={out_dtype}")
+    xt = torch.from_numpy(x).cuda()
+    out = b.fused_normalize(xt, mean, std, 0.5, 0.5, seed=17, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref, _ = oracle.fused_normalize(x, mean, std, 0.5, 0.5, seed=17)
+    P = oracle.params(17, 0, N, H, W, 0.5, 0.5)
+    got = out.cpu().numpy()
+    if out_dtype == 2:
+        assert np.all(got[..., C:].view(np.uint16) == 0)
+        got = np.ascontiguousarray(got[..., :C])
+    check_values(got, ref, str(consts), rne_exact=False, erased=erased_mask(P, H, W))
+
+
 def test_copy_hook(b):
     n = (1 << 20) + 16 * 37
     src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
