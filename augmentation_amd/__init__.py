@@ -13,7 +13,7 @@ synthetic inputs) needs no GPU library.
 """
 _BINDING_NAMES = (
     "fn_params", "fn_params_ex", "fn_fused_normalize", "fn_fused_normalize_ex", "fn_last_error",
-    "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_copy", "fn_test_stream", "FnError", "PARAMS_DTYPE",
+    "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_stream", "FnError", "PARAMS_DTYPE",
     "FN_OUT_FP32", "FN_OUT_FP16", "FN_OUT_FP16_PAD4", "fused_normalize", "sample_params",
 )
 

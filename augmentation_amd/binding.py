@@ -44,7 +44,6 @@ _SIGS = {
     "fn_params_ex": [_u64, _i64, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _f32, _f32, _P, _P],
     "fn_test_erase_dims": [_P, _P, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _P, _P, _P, _P],
     "fn_test_cr_ops": [_i32, _P, _P, _i64, _P, _P],
-    "fn_test_copy": [_P, _P, _i64, _P],
     "fn_test_stream": [_P, _P, _i64, _i32, _P],
 }
 for _name, _args in _SIGS.items():
@@ -54,8 +53,7 @@ _lib.fn_last_error.argtypes = []
 _lib.fn_last_error.restype = ctypes.c_char_p
 
 EXPORTED = ("fn_fused_normalize", "fn_fused_normalize_ex", "fn_params", "fn_params_ex",
-            "fn_last_error", "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_copy",
-            "fn_test_stream")
+            "fn_last_error", "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_stream")
 
 
 class FnError(RuntimeError):
@@ -141,10 +139,6 @@ def fn_test_erase_dims(w_scale, w_ratio, count, H, W, scale_min, scale_max, rati
 
 def fn_test_cr_ops(op, a, b, count, out, stream=None) -> int:
     return _check(_lib.fn_test_cr_ops(op, _addr(a), _addr(b), count, _addr(out), _stream(stream)))
-
-
-def fn_test_copy(src, dst, nbytes, stream=None) -> int:
-    return _check(_lib.fn_test_copy(_addr(src), _addr(dst), nbytes, _stream(stream)))
 
 
 def fn_test_stream(src, dst, in_bytes, widen, stream=None) -> int:

@@ -621,36 +621,12 @@ FN_EXPORT int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev,
   return launch_status("cr_ops_kernel launch");
 }
 
-FN_EXPORT int fn_test_copy(const void* src_dev, void* dst_dev, int64_t bytes, void* stream) {
-  if (bytes < 0 || bytes % 16 != 0) return fail(FN_EINVAL, "bytes must be a multiple of 16");
-  if (((uintptr_t)src_dev | (uintptr_t)dst_dev) & 15u)
-    return fail(FN_EINVAL, "pointers must be 16-byte aligned");
-  if (bytes == 0) return ok();
-  int rc;
-  int dev = -1;
-  if ((rc = check_device_range(src_dev, (size_t)bytes, "src_dev", &dev)) ||
-      (rc = check_device_range(dst_dev, (size_t)bytes, "dst_dev", &dev)))
-    return rc;
-  const uintptr_t s0 = (uintptr_t)src_dev, d0 = (uintptr_t)dst_dev;
-  if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes)
-    return fail(FN_EINVAL, "source and destination overlap");
-  const int64_t vecs = bytes / 16;
-  int64_t blocks = (vecs + fn::kBlock - 1) / fn::kBlock;
-  if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride beyond 64 work-groups per CU
-  fn::copy_kernel<<<(unsigned)blocks, fn::kBlock, 0, (hipStream_t)stream>>>(
-      reinterpret_cast<const uint4*>(src_dev), reinterpret_cast<uint4*>(dst_dev), vecs);
-  return launch_status("copy_kernel launch");
-}
-
 FN_EXPORT int fn_test_stream(const void* src_dev, void* dst_dev, int64_t in_bytes, int32_t widen,
                              void* stream) {
   if (widen != 2 && widen != 4) return fail(FN_EINVAL, "widen must be 2 or 4");
-  const int64_t per_lane = 16 / widen;  // input bytes per lane
-  if (in_bytes < 0 || in_bytes % per_lane != 0)
-    return fail(FN_EINVAL, "in_bytes must be a multiple of %d", (int)per_lane);
-  if (((uintptr_t)src_dev % (uintptr_t)per_lane) != 0 || ((uintptr_t)dst_dev & 15u) != 0)
-    return fail(FN_EINVAL, "src_dev must be %d-byte aligned and dst_dev 16-byte aligned",
-                (int)per_lane);
+  if (in_bytes < 0 || in_bytes % 16 != 0) return fail(FN_EINVAL, "in_bytes must be a multiple of 16");
+  if ((((uintptr_t)src_dev | (uintptr_t)dst_dev) & 15u) != 0)
+    return fail(FN_EINVAL, "src_dev and dst_dev must be 16-byte aligned");
   if (in_bytes > ((int64_t)1 << 40)) return fail(FN_EOVERFLOW, "in_bytes too large");
   if (in_bytes == 0) return ok();
   int rc;
@@ -661,13 +637,13 @@ FN_EXPORT int fn_test_stream(const void* src_dev, void* dst_dev, int64_t in_byte
   const uintptr_t s0 = (uintptr_t)src_dev, d0 = (uintptr_t)dst_dev;
   if (s0 < d0 + (uintptr_t)(in_bytes * widen) && d0 < s0 + (uintptr_t)in_bytes)
     return fail(FN_EINVAL, "source and destination overlap");
-  const int64_t lanes = in_bytes / per_lane;
+  const int64_t lanes = in_bytes / (widen == 2 ? 8 : 16);
   const unsigned grid = blocks_for(lanes, fn::kBlock);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(src_dev);
+  fn::u32x4* dst = reinterpret_cast<fn::u32x4*>(dst_dev);
   if (widen == 2)
-    fn::stream_kernel<2><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(
-        reinterpret_cast<const uint8_t*>(src_dev), reinterpret_cast<fn::u32x4*>(dst_dev), lanes);
+    fn::stream_kernel<2><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(src, dst, lanes);
   else
-    fn::stream_kernel<4><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(
-        reinterpret_cast<const uint8_t*>(src_dev), reinterpret_cast<fn::u32x4*>(dst_dev), lanes);
+    fn::stream_kernel<4><<<grid, fn::kBlock, 0, (hipStream_t)stream>>>(src, dst, lanes);
   return launch_status("stream_kernel launch");
 }

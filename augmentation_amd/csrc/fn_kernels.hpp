@@ -22,8 +22,7 @@
 //   normalize()), stored as fp32 or round-to-nearest-even fp16.
 //   erase_dims_kernel,
 //   cr_ops_kernel,
-//   stream_kernel,
-//   copy_kernel            test and measurement hooks.
+//   stream_kernel          test and measurement hooks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -803,35 +802,42 @@ __global__ void __launch_bounds__(kBlock) cr_ops_kernel(int32_t op, const float*
   out[s] = r;
 }
 
-// The operation's traffic without its arithmetic: every lane reads 16/K
-// bytes and writes them widened to K bytes each (zero-extended) as one
-// 16-byte streaming store, lane-contiguous; K = 2 is the fp16 operation's
-// 1:2 read:write mix, K = 4 the fp32 one's 1:4.  One lane per 16 output
-// bytes, one-shot grid: the shape that moved these mixes fastest on the
-// hardware, so its rate is the practical roof for the fused kernel.
+// The operation's traffic without its arithmetic, in the shape that moved
+// each mix fastest on the hardware, so that its rate is the practical roof
+// for the fused kernels.  Every store is a 16-byte streaming store and every
+// store instruction is lane-contiguous (lane-strided stores run several
+// times slower).
+//   K = 2 (the fp16 operation's 1:2 read:write mix): lane i reads input bytes
+//     8i .. 8i+7 and writes them zero-extended to 16 bits as output vector i:
+//     the output is the input widened in order.
+//   K = 4 (the fp32 operation's 1:4 mix): lane i reads input vector i (16
+//     bytes) and writes its dword k (4 bytes, each zero-extended to 32 bits)
+//     as output vector 4 b + k m + (i - b), where the lane's block of m lanes
+//     starts at lane b.
+// `lanes` = input bytes / 8 (K = 2) or / 16 (K = 4).
 template <int K>
 __global__ void __launch_bounds__(kBlock) stream_kernel(const uint8_t* __restrict__ src,
                                                         u32x4* __restrict__ dst, int64_t lanes) {
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t b0 = (int64_t)blockIdx.x * kBlock;
+  const int64_t i = b0 + threadIdx.x;
   if (i >= lanes) return;
-  u32x4 q;
   if constexpr (K == 2) {
     const uint2 w = reinterpret_cast<const uint2*>(src)[i];
     // v_perm_b32 byte selectors: 0..3 pick bytes of the second operand, 12 gives 0
-    q = u32x4{__builtin_amdgcn_perm(0u, w.x, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.x, 0x0C030C02u),
-              __builtin_amdgcn_perm(0u, w.y, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.y, 0x0C030C02u)};
+    const u32x4 q{__builtin_amdgcn_perm(0u, w.x, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.x, 0x0C030C02u),
+                  __builtin_amdgcn_perm(0u, w.y, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.y, 0x0C030C02u)};
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(dst + i), "v"(q) : "memory");
   } else {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(src)[i];
-    q = u32x4{w & 0xFFu, (w >> 8) & 0xFFu, (w >> 16) & 0xFFu, w >> 24};
+    const int64_t m = min((int64_t)kBlock, lanes - b0);  // lanes of this block
+    const u32x4 w = reinterpret_cast<const u32x4*>(src)[i];
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 q{d[k] & 0xFFu, (d[k] >> 8) & 0xFFu, (d[k] >> 16) & 0xFFu, d[k] >> 24};
+      u32x4* p = dst + 4 * b0 + k * m + threadIdx.x;
+      asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(p), "v"(q) : "memory");
+    }
   }
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(dst + i), "v"(q) : "memory");
-}
-
-__global__ void __launch_bounds__(kBlock) copy_kernel(const uint4* __restrict__ src,
-                                                      uint4* __restrict__ dst, int64_t vecs) {
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x; v < vecs; v += stride)
-    dst[v] = src[v];
 }
 
 }  // namespace fn

@@ -26,7 +26,7 @@ launches between two device synchronisations.
 
 Extra legs: stream_ceiling times the library's streaming reference
 (fn_test_stream: the same read:write mix and byte count with no arithmetic,
-one 16-byte streaming store per lane), the practical roof for the fused
+lane-contiguous 16-byte streaming stores), the practical roof for the fused
 kernel; host_us is the host time per call while the timed launches are
 enqueued; --all adds one line per workload on stderr; --sweep instead prints
 per-batch-size lines for the headline shape (the fused call, the streaming
@@ -235,10 +235,10 @@ def sweep(b, steps: int, warmup: int, prewarm_s: float, sizes) -> None:
     img = w.H * w.W * w.C
     tiny_src = torch.ones(16, dtype=torch.uint8, device="cuda")
     tiny_dst = torch.empty(32, dtype=torch.uint8, device="cuda")
-    floor = time_launches(lambda k: b.fn_test_stream(tiny_src, tiny_dst, 8, 2, stream),
+    floor = time_launches(lambda k: b.fn_test_stream(tiny_src, tiny_dst, 16, 2, stream),
                           max(steps, 1000), warmup, 1, stream, prewarm_s)
     print(json.dumps({"sweep": "launch_floor", "us": round(floor * 1e3, 3),
-                      "what": "fn_test_stream on 8 bytes, back to back"}), flush=True)
+                      "what": "fn_test_stream on 16 bytes, back to back"}), flush=True)
     base = torch.from_numpy(w.make_input()).cuda()
     pts = {"fused": [], "stream": []}
     for N in sizes:

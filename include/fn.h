@@ -195,7 +195,7 @@ const char* fn_last_error(void);
 /* ------------------------------------------------------------------------ */
 /* Test and measurement hooks.  Not part of the operation; exposed so tests  */
 /* can check the building blocks exhaustively and the benchmark can measure  */
-/* a plain copy of known size.  Same conventions as above.                   */
+/* the operation's traffic alone.  Same conventions as above.                */
 /* ------------------------------------------------------------------------ */
 
 /* One erase attempt (page sec. 12) per index s in [0, count): from the area
@@ -217,18 +217,18 @@ int fn_test_erase_dims(const uint32_t* w_scale_dev, const uint32_t* w_ratio_dev,
 int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev, int64_t count,
                    float* out_dev, void* stream);
 
-/* A plain 16-byte-vector device copy of `bytes` bytes (a multiple of 16, both
- * pointers 16-byte aligned, no overlap): the reference kernel for bandwidth
- * and for calibrating hardware byte counters. */
-int fn_test_copy(const void* src_dev, void* dst_dev, int64_t bytes, void* stream);
-
 /* The operation's traffic without its arithmetic, as the practical bandwidth
- * roof of the fused kernels: reads in_bytes from src_dev and writes each byte
- * zero-extended to `widen` bytes (2: the fp16 operation's 1:2 read:write mix,
- * 4: the fp32 one's 1:4), in_bytes * widen bytes in all, as 16-byte streaming
- * stores.  in_bytes a multiple of 16/widen; src_dev aligned to 16/widen
- * bytes, dst_dev to 16; no overlap.  Errors as above (FN_EINVAL for any other
- * widen). */
+ * roof of the fused kernels: reads in_bytes from src_dev and writes every
+ * byte zero-extended to `widen` bytes, in_bytes * widen bytes in all, as
+ * 16-byte streaming stores.
+ *   widen 2 (the fp16 operation's 1:2 read:write mix): the output is the
+ *     input widened to 16 bits, in order.
+ *   widen 4 (the fp32 one's 1:4 mix): per block of 256 input vectors of 16
+ *     bytes starting at vector b (m = min(256, in_bytes/16 - b) vectors in
+ *     the block), dword k of vector v, widened to four 32-bit values, is
+ *     output vector 4b + k*m + (v - b).
+ * in_bytes a multiple of 16; both pointers 16-byte aligned; no overlap.
+ * Errors as above (FN_EINVAL for any other widen). */
 int fn_test_stream(const void* src_dev, void* dst_dev, int64_t in_bytes, int32_t widen,
                    void* stream);
 

@@ -106,9 +106,8 @@ def test_params_and_hooks_validate(b):
     assert L.fn_params(1, 4, 8, 8, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, None, None) == -1  # NULL out
     assert L.fn_test_cr_ops(3, None, None, 1, None, None) == -1
     assert L.fn_test_cr_ops(0, None, None, 0, None, None) == 0
-    assert L.fn_test_copy(None, None, 15, None) == -1
     assert L.fn_test_stream(None, None, 16, 3, None) == -1   # widen must be 2 or 4
-    assert L.fn_test_stream(None, None, 12, 2, None) == -1   # 8-byte multiple for widen 2
+    assert L.fn_test_stream(None, None, 24, 2, None) == -1   # a multiple of 16 bytes
     assert L.fn_test_stream(None, None, 0, 4, None) == 0
     assert L.fn_test_stream(None, None, 16, 2, None) == -1   # NULL buffers
     assert L.fn_test_erase_dims(None, None, 0, 8, 8, 0.02, 0.33, 0.3, 3.3, None, None, None,

@@ -347,16 +347,36 @@ def test_bad_pointers_rejected_without_launch(b):
     assert float(y) == x.numel()
 
 
+def stream_reference(src: np.ndarray, widen: int) -> np.ndarray:
+    """What fn_test_stream writes, from its documented layout: widen 2, the
+    input widened in order; widen 4, per block of up to 256 input vectors of
+    16 bytes, dword k of every vector (its 4 bytes, each zero-extended) forms
+    the block's k-th run of output vectors."""
+    if widen == 2:
+        return src.astype(np.uint16)
+    vec = src.reshape(-1, 16)
+    out = []
+    for b in range(0, len(vec), 256):
+        blk = vec[b:b + 256]
+        parts = blk.reshape(len(blk), 4, 4).astype(np.uint32)
+        out.append(parts.transpose(1, 0, 2).reshape(-1))
+    return np.concatenate(out)
+
+
 @pytest.mark.parametrize("widen", [2, 4])
 def test_stream_hook(b, widen):
-    """fn_test_stream writes every input byte zero-extended to `widen` bytes."""
+    """fn_test_stream writes every input byte zero-extended to `widen` bytes,
+    in its documented block layout, including a partial last block, and
+    nothing beyond its output."""
     n = (1 << 20) + 16 * 37
     src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
-    dst = torch.full((n * widen,), 0xA5, dtype=torch.uint8, device="cuda")
+    dst = torch.full((n * widen + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
     b.fn_test_stream(src, dst, n, widen)
     torch.cuda.synchronize()
-    got = dst.cpu().numpy().view(np.uint16 if widen == 2 else np.uint32)
-    np.testing.assert_array_equal(got, src.cpu().numpy().astype(got.dtype))
+    host = dst.cpu().numpy()
+    assert np.all(host[n * widen:] == 0xA5)
+    got = host[:n * widen].view(np.uint16 if widen == 2 else np.uint32)
+    np.testing.assert_array_equal(got, stream_reference(src.cpu().numpy(), widen))
 
 
 # Constants whose single-fma result is not always the correctly rounded one:
@@ -387,15 +407,6 @@ def test_tiles_kernel_with_cancelling_constants(b, consts, out_dtype):
         assert np.all(got[..., C:].view(np.uint16) == 0)
         got = np.ascontiguousarray(got[..., :C])
     check_values(got, ref, str(consts), rne_exact=False, erased=erased_mask(P, H, W))
-
-
-def test_copy_hook(b):
-    n = (1 << 20) + 16 * 37
-    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
-    dst = torch.zeros_like(src)
-    b.fn_test_copy(src, dst, n)
-    torch.cuda.synchronize()
-    assert torch.equal(src, dst)
 
 
 def test_batch_beyond_4gib(b):
