@@ -32,6 +32,27 @@ FLAGS = [
 ]
 
 
+CPU_SOURCES = [os.path.join(HERE, "cpu", "fn_cpu.cpp")]
+CPU_LIB_PATH = os.path.join(HERE, "libfn_cpu.so")
+# the page's host method: SSE4.1 (with its SSSE3 byte shuffle) + F16C;
+# -ffp-contract=off keeps its product and difference separately rounded
+CPU_FLAGS = ["-std=c++17", "-O3", "-msse4.1", "-mf16c", "-ffp-contract=off", "-fPIC", "-shared",
+             "-fvisibility=hidden", "-Wall", "-Wextra", f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def build_cpu(verbose: bool = False) -> str:
+    """Compile the host SSE4.1/F16C library (always recompiles)."""
+    tmp = CPU_LIB_PATH + ".tmp"
+    cmd = ["g++", *CPU_FLAGS, *CPU_SOURCES, "-o", tmp, "-lpthread"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("g++ failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, CPU_LIB_PATH)
+    return CPU_LIB_PATH
+
+
 def build(verbose: bool = False) -> str:
     """Compile the library (always recompiles) and return its path."""
     tmp = LIB_PATH + ".tmp"
@@ -51,3 +72,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_cpu(verbose=True))

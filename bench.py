@@ -18,7 +18,8 @@ Prints ONE JSON line:
              rocprofv3 counter summary, if it was taken on the current
              build of libfn.so (else null)
   cpu_baseline  the oracle (plain C loops, fp32 output) timed on this
-             host's cores over a bounded sample of the same workload.
+             host's cores over a bounded sample of the same workload;
+             cpu_simd the page's own host method (SSE4.1 + F16C) beside it.
 
 Timing: about --prewarm-seconds of untimed launches (the GPU clocks down
 while the host builds inputs), --warmup untimed launches, then --steps timed
@@ -306,6 +307,40 @@ def cpu_baseline(w, budget_s: float) -> dict:
             "single_thread_images_per_s": round(one / el1, 2)}
 
 
+def cpu_simd_rate(w, budget_s: float) -> dict:
+    """The page's own method on the host (libfn_cpu.so: SSE4.1 + F16C, one
+    image per worker call) on the same workload and output type, on this
+    host's cores for about budget_s seconds, then on one thread for about a
+    fifth of that."""
+    import numpy as np
+    from augmentation_amd import cpu_simd
+    threads = host_threads()
+    x = w.window(w.make_input()) if w.src_h else w.make_input()
+    dt = np.float32 if w.out_dtype == 0 else np.float16
+    out = np.empty(w.out_shape, dt)
+
+    def run(batch, t):
+        cpu_simd.fused_normalize(batch, w.mean, w.std, w.flip_p, w.erase_p, w.scale, w.ratio,
+                                 seed=w.seeds[0], out_dtype=w.out_dtype, threads=t,
+                                 out=out[:len(batch)])
+
+    reps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        run(x, threads)
+        reps += 1
+    el = time.perf_counter() - t0
+    one, t1 = 0, time.perf_counter()
+    while time.perf_counter() - t1 < budget_s / 5:
+        run(x[:8], 1)
+        one += 8
+    el1 = time.perf_counter() - t1
+    return {"value": round(reps * w.N / el, 2), "unit": "images/s", "cores": min(threads, w.N),
+            "kind": "the page's host method (SSE4.1 + F16C, libfn_cpu.so)",
+            "sample": f"{reps} x the {w.N}-image batch, {OUT_NAMES[w.out_dtype]} output, "
+                      f"{el:.1f} s wall; CPU: {cpu_model()}",
+            "single_thread_images_per_s": round(one / el1, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,6 +430,7 @@ def main() -> int:
                   file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_simd"] = cpu_simd_rate(w, args.cpu_seconds / 2)
     print(json.dumps(line), flush=True)
     return 0
 
