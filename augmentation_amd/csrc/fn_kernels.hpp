@@ -205,6 +205,17 @@ __device__ __forceinline__ void load_group(const uint8_t* __restrict__ p, uint32
   }
 }
 
+// One 16-byte store with the system-scope streaming policy (sc0 sc1 nt),
+// which no compiler builtin expresses.  The compiler does not know that the
+// asm is a store, so it does not keep the data VGPRs of a store wider than
+// 8 bytes unwritten for the two wait states this chip needs before a VALU
+// instruction may overwrite them; the s_nop after the store provides them
+// (without it a value computed right after the store can reach memory in
+// place of the stored one).
+__device__ __forceinline__ void stream_store16(u32x4* p, u32x4 q) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" ::"v"(p), "v"(q) : "memory");
+}
+
 // Stores NE output values as 16-, 8- or 4-byte vectors.
 // kStream: 16-byte vectors with the streaming policy FN_NT_STORE (for
 // lane-contiguous stores); otherwise plain stores (lane-strided patterns,
@@ -233,7 +244,7 @@ __device__ __forceinline__ void store_group(OutT* __restrict__ dst, const float 
       if constexpr (kStream && FN_NT_STORE == 1) {
         __builtin_nontemporal_store(q, p);
       } else if constexpr (kStream && FN_NT_STORE == 2) {
-        asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(p), "v"(q) : "memory");
+        stream_store16(p, q);
       } else {
         *p = q;
       }
@@ -826,7 +837,7 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(const uint8_t* __restric
     // v_perm_b32 byte selectors: 0..3 pick bytes of the second operand, 12 gives 0
     const u32x4 q{__builtin_amdgcn_perm(0u, w.x, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.x, 0x0C030C02u),
                   __builtin_amdgcn_perm(0u, w.y, 0x0C010C00u), __builtin_amdgcn_perm(0u, w.y, 0x0C030C02u)};
-    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(dst + i), "v"(q) : "memory");
+    stream_store16(dst + i, q);
   } else {
     const int64_t m = min((int64_t)kBlock, lanes - b0);  // lanes of this block
     const u32x4 w = reinterpret_cast<const u32x4*>(src)[i];
@@ -834,8 +845,7 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(const uint8_t* __restric
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const u32x4 q{d[k] & 0xFFu, (d[k] >> 8) & 0xFFu, (d[k] >> 16) & 0xFFu, d[k] >> 24};
-      u32x4* p = dst + 4 * b0 + k * m + threadIdx.x;
-      asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" ::"v"(p), "v"(q) : "memory");
+      stream_store16(dst + 4 * b0 + k * m + threadIdx.x, q);
     }
   }
 }
