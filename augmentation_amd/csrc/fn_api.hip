@@ -519,6 +519,14 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
     a.div_row_out = make_fast_div((uint32_t)row_out);
     a.div_h = make_fast_div((uint32_t)H);
     a.div_tpi = make_fast_div((uint32_t)a.tiles_per_image);
+    {
+      const int32_t chunk = out_dtype == FN_OUT_FP32 ? 4 : 8;  // outputs per 16-byte store
+      const int32_t threads = out_dtype == FN_OUT_FP32 ? fn::tiles_threads<float>()
+                                                       : fn::tiles_threads<_Float16>();
+      const int32_t cpr = (int32_t)(row_out / chunk);
+      a.div_cpr = make_fast_div((uint32_t)cpr);
+      a.rows_per_pass = cpr <= threads ? threads / cpr : 0;
+    }
     const bool comp = !single_fma_exact(a, C, out_dtype);
     launch_tiles(a, C, out_dtype, comp, (unsigned)a.total_tiles,
                  tiles_lds_bytes(dev, a.lds_buffer_bytes), st);

@@ -119,6 +119,10 @@ struct FusedArgs {
   FastDiv div_row_out;        // by W * oc
   FastDiv div_h;              // by H
   FastDiv div_tpi;            // by tiles_per_image
+  // tiles kernel lanes: output chunks per row (W * oc / E) and rows per pass
+  // (work-group size / chunks per row, when at least 1)
+  FastDiv div_cpr;
+  int32_t rows_per_pass;
   // 1 / (255 std_c) = mul + mul_lo and -mean_c / std_c = nsub + nsub_lo,
   // each the double value split into an fp32 pair (see normalize())
   float mul[4], mul_lo[4];
@@ -360,6 +364,8 @@ struct Tile {
   int64_t n_first;  // first image
   int32_t h0;       // first row in that image
   int32_t rows;     // rows in the tile (across images when several)
+  int32_t images;   // images the tile touches
+  int64_t pixel;    // index of the tile's first pixel, (n_first * H + h0) * W
   int64_t start;    // offset of the tile's first byte in the compact layout
   int32_t len;      // bytes of the tile in the compact layout (rows * W * C)
 };
@@ -372,12 +378,15 @@ __device__ __forceinline__ Tile tile_at(const FusedArgs& a, uint32_t t) {
     T.n_first = n;
     T.h0 = (int32_t)(t - n * (uint32_t)a.tiles_per_image) * a.rows_per_tile;
     T.rows = min(a.rows_per_tile, a.H - T.h0);
+    T.images = 1;
   } else {
     T.n_first = (int64_t)t * a.images_per_tile;
     T.h0 = 0;
-    T.rows = (int32_t)min((int64_t)a.images_per_tile, a.N - T.n_first) * a.H;
+    T.images = (int32_t)min((int64_t)a.images_per_tile, a.N - T.n_first);
+    T.rows = T.images * a.H;
   }
-  T.start = (T.n_first * a.H + T.h0) * (int64_t)row;
+  T.pixel = (T.n_first * a.H + T.h0) * (int64_t)a.W;
+  T.start = T.pixel * a.C;
   T.len = T.rows * row;
   return T;
 }
@@ -540,10 +549,22 @@ __device__ __forceinline__ void load_tile_waves(const FusedArgs& a, const Tile& 
   const int32_t head = (int32_t)(t_lo - gbase);
   const int32_t ngran = (head + T.len + 15) >> 4;
   const bool interior = gbase >= in_lo && gbase + 16 * (uintptr_t)ngran <= in_hi;
+  if (interior) {
+    // every granule lies inside the buffer (all tiles but the edges of an
+    // unaligned batch): a wavefront-uniform base plus the lane's 16 bytes
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(gbase) + 16 * lane;
+    for (int32_t batch = 64 * index; batch < ngran; batch += 64 * count) {
+      if (batch + lane < ngran)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + 16 * batch),
+                                         (__attribute__((address_space(3))) void*)(buf + 16 * batch),
+                                         16, 0, 0);
+    }
+    return;
+  }
   for (int32_t batch = 64 * index; batch < ngran; batch += 64 * count) {
     const int32_t g = batch + lane;
     const uintptr_t A = gbase + 16 * (uintptr_t)g;
-    if (g < ngran && (interior || (A >= in_lo && A + 16 <= in_hi))) {
+    if (g < ngran && A >= in_lo && A + 16 <= in_hi) {
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(A),
                                        (__attribute__((address_space(3))) void*)(buf + 16 * batch),
                                        16, 0, 0);
@@ -639,7 +660,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
   const Tile T = tile_at(a, blockIdx.x);
-  const int n_count = (T.rows - 1) / a.H + 1;
+  const int n_count = T.images;
   const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
   const int32_t draw_waves = min(kWaves, (n_count + 3) >> 2);
   // every wavefront issues its share of the tile's DMA loads first; the
@@ -666,14 +687,14 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   const int32_t row_out = a.W * OC;   // output elements of a row
   const int32_t cpr = row_out / E;    // chunks per row
   const int ct = (int)threadIdx.x;
-  OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + (T.start / C) * OC;
+  OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out) + T.pixel * OC;
   // A tile of one image reads its decision record into registers once;
   // tiles of several images look up each row's record.
   const bool single = a.images_per_tile == 1;
   const SampleParams P0 = s_params[0];
   if (cpr <= kThreads) {
-    const int32_t rpi = kThreads / cpr;  // rows per pass
-    const int32_t slot_row = ct / cpr;
+    const int32_t rpi = a.rows_per_pass;  // kThreads / cpr
+    const int32_t slot_row = (int32_t)fast_div((uint32_t)ct, a.div_cpr);
     if (slot_row < rpi) {
       const Setup cs(a, (ct - slot_row * cpr) * E);
       if (single) {
