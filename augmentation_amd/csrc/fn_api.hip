@@ -251,6 +251,38 @@ void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, bool comp, unsig
     launch_tiles_k<false>(a, C, out_dtype, grid, lds, st);
 }
 
+template <int C, bool kComp>
+void launch_flat_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t lds,
+                   hipStream_t st) {
+  if (out_dtype == FN_OUT_FP32)
+    fn::fused_flat_kernel<C, float, false, kComp><<<grid, fn::tiles_threads<float>(), lds, st>>>(a);
+  else if (out_dtype == FN_OUT_FP16_PAD4)
+    fn::fused_flat_kernel<C, _Float16, true, kComp>
+        <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
+  else
+    fn::fused_flat_kernel<C, _Float16, false, kComp>
+        <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
+}
+
+template <bool kComp>
+void launch_flat_k(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
+                   hipStream_t st) {
+  switch (C) {
+    case 1: launch_flat_c<1, kComp>(a, out_dtype, grid, lds, st); break;
+    case 2: launch_flat_c<2, kComp>(a, out_dtype, grid, lds, st); break;
+    case 3: launch_flat_c<3, kComp>(a, out_dtype, grid, lds, st); break;
+    default: launch_flat_c<4, kComp>(a, out_dtype, grid, lds, st); break;
+  }
+}
+
+void launch_flat(const fn::FusedArgs& a, int C, int out_dtype, bool comp, unsigned grid,
+                 size_t lds, hipStream_t st) {
+  if (comp)
+    launch_flat_k<true>(a, C, out_dtype, grid, lds, st);
+  else
+    launch_flat_k<false>(a, C, out_dtype, grid, lds, st);
+}
+
 // Bits of the binary16 value nearest to v (ties to even), as the GPU's
 // float-to-half conversion gives them.
 uint16_t half_bits_rne(float v) {
@@ -355,9 +387,10 @@ int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elem
     tile_bytes = r * row;
   }
   // contiguous: the tile's bytes plus the partial granules at both ends;
-  // strided: one 16-byte-granule slot per row
+  // strided: one 16-byte-granule slot per row, and 16 bytes of slack for the
+  // aligned dword reads that run up to 3 bytes past the last row's end
   const int64_t tile_rows = a->images_per_tile == 1 ? a->rows_per_tile : a->images_per_tile * H;
-  const int64_t lds = row_slot > 0 ? tile_rows * row_slot : (tile_bytes + 32 + 15) / 16 * 16;
+  const int64_t lds = row_slot > 0 ? tile_rows * row_slot + 16 : (tile_bytes + 32 + 15) / 16 * 16;
   if (lds > fn::kTileBytesMax + 64) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
   if (a->total_tiles > 0x7FFFFFFF) return fail(FN_EOVERFLOW, "grid size limit exceeded");
   a->lds_buffer_bytes = (int32_t)lds;
@@ -504,8 +537,7 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
   a.in_image_stride = image_stride;
   a.strided = strided ? 1 : 0;
   const int64_t row_out = (int64_t)W * oc;
-  if ((uintptr_t)out_dev % 16 == 0 && row_out % (16 / out_bytes) == 0 &&
-      row <= fn::kTileBytesMax) {
+  if (row <= fn::kTileBytesMax) {
     int cus = 0;
     rc = device_cu_count(dev, &cus);
     if (rc) return rc;
@@ -523,14 +555,23 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
       const int32_t chunk = out_dtype == FN_OUT_FP32 ? 4 : 8;  // outputs per 16-byte store
       const int32_t threads = out_dtype == FN_OUT_FP32 ? fn::tiles_threads<float>()
                                                        : fn::tiles_threads<_Float16>();
+      // chunks per row: 0 for rows shorter than one vector, which only the
+      // flat kernel takes
       const int32_t cpr = (int32_t)(row_out / chunk);
-      a.div_cpr = make_fast_div((uint32_t)cpr);
-      a.rows_per_pass = cpr <= threads ? threads / cpr : 0;
+      a.div_cpr = make_fast_div((uint32_t)std::max<int32_t>(cpr, 1));
+      a.rows_per_pass = cpr >= 1 && cpr <= threads ? threads / cpr : 0;
     }
     const bool comp = !single_fma_exact(a, C, out_dtype);
-    launch_tiles(a, C, out_dtype, comp, (unsigned)a.total_tiles,
-                 tiles_lds_bytes(dev, a.lds_buffer_bytes), st);
-    return launch_status("fused_tiles_kernel launch");
+    const size_t lds = tiles_lds_bytes(dev, a.lds_buffer_bytes);
+    // the tiles kernel's lanes need whole 16-byte vectors per row from a
+    // 16-byte aligned output; any other element-aligned output takes the
+    // flat layout
+    if ((uintptr_t)out_dev % 16 == 0 && row_out % (16 / out_bytes) == 0) {
+      launch_tiles(a, C, out_dtype, comp, (unsigned)a.total_tiles, lds, st);
+      return launch_status("fused_tiles_kernel launch");
+    }
+    launch_flat(a, C, out_dtype, comp, (unsigned)a.total_tiles, lds, st);
+    return launch_status("fused_flat_kernel launch");
   }
   const int px = out_dtype == FN_OUT_FP16_PAD4 || strided
                      ? 0

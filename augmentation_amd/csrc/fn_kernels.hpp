@@ -9,15 +9,22 @@
 //                          global-to-LDS DMA while the tile's decisions are
 //                          drawn; each lane then writes 16-byte vectors of a
 //                          row, reading flipped sources from LDS.
-//   fused_grouped_kernel   the same operation when the tiles kernel does not
-//                          apply but the width is a multiple of a pixel group
-//                          PX: each lane owns groups of PX consecutive pixels
-//                          of one row; a flipped group reads the mirrored
-//                          group of the same row and reverses the pixel order
-//                          in registers, keeping the channel order; a group
-//                          wholly inside the erase rectangle reads nothing.
-//   fused_generic_kernel   the same operation for any shape and alignment,
-//                          one element at a time.
+//   fused_flat_kernel      the same staging for the other outputs whose rows
+//                          fit a tile: rows that end inside a 16-byte vector,
+//                          or an output aligned only to its element size;
+//                          lanes take the buffer's aligned 16-byte vectors,
+//                          and the few that hold a row start are done element
+//                          by element in a second pass.
+//   fused_grouped_kernel   rows too wide for a tile, when the width is a
+//                          multiple of a pixel group PX and the output is
+//                          16-byte aligned: each lane owns groups of PX
+//                          consecutive pixels of one row; a flipped group
+//                          reads the mirrored group of the same row and
+//                          reverses the pixel order in registers, keeping the
+//                          channel order; a group wholly inside the erase
+//                          rectangle reads nothing.
+//   fused_generic_kernel   any other row too wide for a tile, one element at
+//                          a time.
 //   Values are (x/255 - mean)/std from fp32 constant pairs (see
 //   normalize()), stored as fp32 or round-to-nearest-even fp16.
 //   erase_dims_kernel,
@@ -449,9 +456,10 @@ struct ChunkSetup {
 
   // Outputs of this lane's E elements of one row (LDS row start `row_lds`,
   // image row h, the image's decisions P).  kSrc says how the source bytes
-  // are read: kSrcFlip mirrored bytes (P.flip set), kSrcAligned two dwords
-  // (row_lds + x0 4-byte aligned), kSrcBytes single bytes; kSrcAny decides
-  // per call.
+  // are read: kSrcFlip mirrored bytes (P.flip set), kSrcAligned E/4 dwords
+  // (row_lds + x0 4-byte aligned), kSrcBytes E/4 + 1 aligned dwords shifted
+  // into place (any alignment; reads up to 3 bytes past the row, which the
+  // staging buffer's slack covers); kSrcAny decides per call.
   template <int kSrc = kSrcAny>
   __device__ __forceinline__ void values(const uint8_t* s_tile, int32_t row_lds,
                                          const SampleParams& P, int32_t h, float (&v)[E]) const {
@@ -469,8 +477,17 @@ struct ChunkSetup {
 #pragma unroll
       for (int k = 0; k < E; ++k) x[k] = (float)((wv[k >> 2] >> (8 * (k & 3))) & 0xFFu);
     } else {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(s_tile + (src & ~3));
+      const uint32_t sh = (uint32_t)src & 3u;
+      uint32_t wa[E / 4 + 1];
 #pragma unroll
-      for (int k = 0; k < E; ++k) x[k] = (float)s_tile[src + k];
+      for (int q = 0; q <= E / 4; ++q) wa[q] = w[q];
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        // byte k of the window: v_alignbyte_b32 takes 4 bytes of hi:lo at a byte shift
+        const uint32_t d = __builtin_amdgcn_alignbyte(wa[(k >> 2) + 1], wa[k >> 2], sh);
+        x[k] = (float)((d >> (8 * (k & 3))) & 0xFFu);
+      }
     }
 #pragma unroll
     for (int k = 0; k < E; ++k)
@@ -635,17 +652,46 @@ constexpr int tiles_threads() {
   return sizeof(OutT) == 2 ? FN_TILE_THREADS_F16 : 512;
 }
 
-// The fused pass, one tile per work-group (grid = total_tiles).  Every
-// wavefront first issues its share of the tile's global-to-LDS DMA loads;
-// then the first ceil(images / 4) wavefronts draw the decisions of the
-// tile's images (a 16-lane group per image) while the loads are in flight.
-// After one barrier every lane makes E = 16/sizeof(OutT) consecutive output
-// elements of a row at a time (two whole 4-channel pixels when kPad4) and
-// stores them as one 16-byte vector, lane-contiguous across the wavefront.
-// A tile of one image reads its decisions into scalar registers and picks
-// the way its source bytes are read (mirrored, aligned dwords or bytes) once.
-// Many small independent work-groups per compute unit hide the memory
-// latency.
+// Stages tile T in LDS and its images' decisions in s_params, for the tiles
+// kernels: every wavefront issues its share of the tile's global-to-LDS DMA
+// loads first; then the first ceil(images / 4) wavefronts draw the decisions
+// of the tile's images (a 16-lane group per image) while the loads are in
+// flight.  Ends with a barrier, after which the whole tile is in LDS.
+template <int kWaves>
+__device__ __forceinline__ void stage_tile(const FusedArgs& a, const Tile& T, uint8_t* s_lds,
+                                           SampleParams* s_params) {
+  const int n_count = T.images;
+  const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+  const int32_t draw_waves = min(kWaves, (n_count + 3) >> 2);
+  if (a.strided)
+    load_tile_rows_waves(a, T, s_lds, wave, kWaves);
+  else
+    load_tile_waves(a, T, s_lds, wave, kWaves);
+  if (wave < draw_waves) {
+    const int slot = (int)(threadIdx.x >> 4);
+    const SampleParams p = draw_sample_params16(a.draw, (uint64_t)(T.n_first + slot));
+    if ((threadIdx.x & 15u) == 0 && slot < n_count) s_params[slot] = p;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's DMA loads have landed
+  __syncthreads();
+}
+
+// LDS offset of the first byte of row r of a staged tile (head = the offset
+// of a compact tile's first byte, row = W * C).
+__device__ __forceinline__ int32_t staged_row(const FusedArgs& a, const Tile& T, int32_t head,
+                                              int32_t row, int32_t r) {
+  if (a.strided) return r * a.row_slot + (int32_t)(tile_row_src(a, T, r) & 15u);
+  return head + r * row;
+}
+
+// The fused pass, one tile per work-group (grid = total_tiles): the tile is
+// staged (stage_tile), then every lane makes E = 16/sizeof(OutT) consecutive
+// output elements of a row at a time (two whole 4-channel pixels when kPad4)
+// and stores them as one 16-byte vector, lane-contiguous across the
+// wavefront.  A tile of one image reads its decisions into scalar registers
+// and picks the way its source bytes are read (mirrored, aligned dwords or
+// bytes) once.  Many small independent work-groups per compute unit hide the
+// memory latency.
 // Requires W*OC a multiple of E (OC = 4 when kPad4, else C) and a 16-byte
 // aligned output; the input may be compact or strided (a.strided).
 template <int C, typename OutT, bool kPad4, bool kComp>
@@ -660,30 +706,11 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
   const Tile T = tile_at(a, blockIdx.x);
-  const int n_count = T.images;
-  const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-  const int32_t draw_waves = min(kWaves, (n_count + 3) >> 2);
-  // every wavefront issues its share of the tile's DMA loads first; the
-  // drawing wavefronts then draw while the loads are in flight
-  if (a.strided)
-    load_tile_rows_waves(a, T, s_lds, wave, kWaves);
-  else
-    load_tile_waves(a, T, s_lds, wave, kWaves);
-  if (wave < draw_waves) {
-    const int slot = (int)(threadIdx.x >> 4);
-    const SampleParams p = draw_sample_params16(a.draw, (uint64_t)(T.n_first + slot));
-    if ((threadIdx.x & 15u) == 0 && slot < n_count) s_params[slot] = p;
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's DMA loads have landed
-  __syncthreads();
+  stage_tile<kWaves>(a, T, s_lds, s_params);
 
   const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
   const int32_t row = a.W * C;        // input bytes of a row
-  // LDS offset of the first byte of tile row r
-  auto row_lds = [&](int32_t r) -> int32_t {
-    if (a.strided) return r * a.row_slot + (int32_t)(tile_row_src(a, T, r) & 15u);
-    return head + r * row;
-  };
+  auto row_lds = [&](int32_t r) -> int32_t { return staged_row(a, T, head, row, r); };
   const int32_t row_out = a.W * OC;   // output elements of a row
   const int32_t cpr = row_out / E;    // chunks per row
   const int ct = (int)threadIdx.x;
@@ -765,6 +792,146 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       float v[E];
       cq.values(s_lds, row_lds((int32_t)r), P, h, v);
       store_group<OutT, E, true>(out + off, v);
+    }
+  }
+}
+
+// Normalized value of input byte x in channel c (a lane-varying c < C).
+template <int C, bool kComp>
+__device__ __forceinline__ float normalize_channel(const FusedArgs& a, float x, int32_t c) {
+  float m = a.mul[0], ml = a.mul_lo[0], n = a.nsub[0], nl = a.nsub_lo[0];
+#pragma unroll
+  for (int cc = 1; cc < C; ++cc) {
+    m = c == cc ? a.mul[cc] : m;
+    ml = c == cc ? a.mul_lo[cc] : ml;
+    n = c == cc ? a.nsub[cc] : n;
+    nl = c == cc ? a.nsub_lo[cc] : nl;
+  }
+  return normalize<kComp>(x, m, ml, n, nl);
+}
+
+// Elements l0 .. l0 + E - 1 of a staged tile's outputs (l0 relative to the
+// tile's first output, count outputs in all), one at a time; elements
+// outside the tile are left 0.
+template <int C, int OC, int E, bool kComp>
+__device__ __forceinline__ void flat_elements(const FusedArgs& a, const Tile& T,
+                                              const uint8_t* s_lds, const SampleParams* s_params,
+                                              int32_t head, int32_t l0, int32_t count,
+                                              float (&v)[E]) {
+  const int32_t row = a.W * C;
+  const int32_t row_out = a.W * OC;
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    const int32_t l = l0 + k;
+    v[k] = 0.0f;
+    if (l < 0 || l >= count) continue;
+    const int32_t r = (int32_t)fast_div((uint32_t)l, a.div_row_out);
+    const int32_t x = l - r * row_out;
+    const int32_t w = x / OC;
+    const int32_t c = x - w * OC;
+    uint32_t slot;
+    int32_t h;
+    tile_row_image(a, T, T.n_first, r, &slot, &h);
+    const SampleParams P = s_params[slot];
+    const bool erased = P.erase && h >= P.i && h < P.i + P.eh && w >= P.j && w < P.j + P.ew;
+    if (c < C && !erased) {
+      const int32_t sw = P.flip ? a.W - 1 - w : w;
+      const float xb = (float)s_lds[staged_row(a, T, head, row, r) + sw * C + c];
+      v[k] = normalize_channel<C, kComp>(a, xb, c);
+    }
+  }
+}
+
+// The fused pass for outputs that the lane layout of fused_tiles_kernel does
+// not fit: rows of W*OC outputs that are not a whole number of 16-byte
+// vectors, or an output aligned only to its element size.  The tile is
+// staged as there.  Its outputs are the contiguous elements [F0, F1) of the
+// output, covered by the 16-byte-aligned vectors of the output buffer.
+// A vector inside one row (and, when kPad4, starting at a pixel) is one
+// chunk, evaluated as in fused_tiles_kernel with its own lane setup; the
+// lanes take those first, one vector each in turn.  The other vectors hold
+// a row start (or the tile's end) at an element other than their first: a
+// second pass walks the tile's row starts, one per lane, and evaluates each
+// such vector element by element, so that the few of them do not hold up
+// whole wavefronts of the first pass.  Only the tile's own elements are
+// stored: the tile next to it stores the rest of a vector they share, so no
+// byte is written twice.
+template <int C, typename OutT, bool kPad4, bool kComp>
+__global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(FusedArgs a) {
+  constexpr int kThreads = tiles_threads<OutT>();
+  constexpr int kWaves = kThreads / 64;
+  constexpr int E = 16 / (int)sizeof(OutT);
+  constexpr int OC = kPad4 ? 4 : C;
+  using Setup = typename std::conditional<kPad4, Pad4Chunk<C, kComp>, ChunkSetup<C, E, kComp>>::type;
+  extern __shared__ __align__(16) uint8_t s_lds[];
+  __shared__ SampleParams s_params[kMaxImagesPerBlock];
+
+  const Tile T = tile_at(a, blockIdx.x);
+  stage_tile<kWaves>(a, T, s_lds, s_params);
+
+  const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
+  const int32_t row = a.W * C;
+  const int32_t row_out = a.W * OC;
+  const int32_t count = T.rows * row_out;  // outputs of the tile
+  // element e of the output lies at out + e * sizeof(OutT); vector k of the
+  // buffer holds elements k*E - mu .. k*E - mu + E - 1
+  const int32_t mu = (int32_t)(((uintptr_t)a.out & 15u) / sizeof(OutT));
+  const int64_t f0 = T.pixel * OC;                    // the tile's first output
+  const int64_t k0 = (f0 + mu) / E;                   // first vector it overlaps
+  const int32_t nvec = (int32_t)((f0 + count + mu + E - 1) / E - k0);
+  // padded outputs off a pixel boundary: no vector starts at a pixel
+  const bool all_elements = kPad4 && (mu & 3) != 0;
+  OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out);
+
+  for (int32_t q = (int32_t)threadIdx.x; q < nvec; q += kThreads) {
+    const int64_t e0 = (k0 + q) * E - mu;
+    const int32_t l0 = (int32_t)(e0 - f0);
+    float v[E];
+    if (all_elements) {
+      flat_elements<C, OC, E, kComp>(a, T, s_lds, s_params, head, l0, count, v);
+      if (l0 >= 0 && l0 + E <= count) {
+        store_group<OutT, E, true>(out + e0, v);
+      } else {
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+          if (l0 + k >= 0 && l0 + k < count) out[e0 + k] = to_out<OutT>(v[k]);
+      }
+      continue;
+    }
+    if (l0 < 0 || l0 + E > count) continue;  // an end of the tile: second pass
+    const int32_t r = (int32_t)fast_div((uint32_t)l0, a.div_row_out);
+    const int32_t x0 = l0 - r * row_out;
+    if (x0 + E > row_out) continue;  // holds the next row's start: second pass
+    uint32_t slot;
+    int32_t h;
+    tile_row_image(a, T, T.n_first, r, &slot, &h);
+    const Setup cs(a, x0);
+    cs.values(s_lds, staged_row(a, T, head, row, r), s_params[slot], h, v);
+    store_group<OutT, E, true>(out + e0, v);
+  }
+  if (all_elements) return;
+
+  // second pass: the vector holding the start of row b (b = T.rows: the
+  // tile's end) when that is not its first element; a vector holding
+  // several row starts is done at the first of them
+  for (int32_t b = (int32_t)threadIdx.x; b <= T.rows; b += kThreads) {
+    const int64_t e = f0 + (int64_t)b * row_out + mu;  // shifted element index
+    if (e % E == 0) continue;
+    const int64_t kv = e / E;
+    if (b > 0) {
+      const int64_t ep = e - row_out;
+      if (ep % E != 0 && ep / E == kv) continue;
+    }
+    const int64_t e0 = kv * E - mu;
+    const int32_t l0 = (int32_t)(e0 - f0);
+    float v[E];
+    flat_elements<C, OC, E, kComp>(a, T, s_lds, s_params, head, l0, count, v);
+    if (l0 >= 0 && l0 + E <= count) {
+      store_group<OutT, E, true>(out + e0, v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < E; ++k)
+        if (l0 + k >= 0 && l0 + k < count) out[e0 + k] = to_out<OutT>(v[k]);
     }
   }
 }

@@ -67,8 +67,9 @@ PAD4_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1,
 @pytest.mark.parametrize("shape", PAD4_SHAPES)
 @pytest.mark.parametrize("out_aligned", [True, False])
 def test_pad4_edge_shapes_with_guards(b, shape, out_aligned):
-    """Odd and even widths (even widths take the tiles kernel, odd ones the
-    element-wise one), rows wider than one pass of the lanes, the input at a
+    """Odd and even widths (even widths at a 16-byte aligned output take the
+    tiles kernel, the rest the flat one), rows wider than one pass of the
+    lanes, the input at a
     byte offset in 1..7, the output 16-byte aligned or only 2-byte aligned,
     and guard bands around the output."""
     N, H, W, C = shape

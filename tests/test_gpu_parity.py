@@ -180,7 +180,10 @@ EDGE_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1,
                (2, 4, 8192, 1), (1, 600, 6, 3), (9, 28, 28, 1), (64, 32, 32, 3),
                (2, 3, 1024, 3), (2, 5, 700, 4), (40, 8, 8, 2), (3, 64, 48, 3),
                # rows wider than the largest LDS tile (24 KB): the pixel-group
-               # kernel (W a multiple of 8) and the element-wise one
+               # kernel (W a multiple of 8, aligned output) and the element-wise
+               # one; the other shapes take the tiles kernel or, when a row ends
+               # inside a 16-byte vector or the output is only element aligned,
+               # the flat one
                (1, 3, 9000, 3), (1, 2, 9001, 3)]
 
 
