@@ -388,7 +388,8 @@ int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elem
   }
   // contiguous: the tile's bytes plus the partial granules at both ends;
   // strided: one 16-byte-granule slot per row, and 16 bytes of slack for the
-  // aligned dword reads that run up to 3 bytes past the last row's end
+  // aligned dword reads that run up to 10 bytes past the last row's end (the
+  // contiguous layout's 32 extra bytes cover them too)
   const int64_t tile_rows = a->images_per_tile == 1 ? a->rows_per_tile : a->images_per_tile * H;
   const int64_t lds = row_slot > 0 ? tile_rows * row_slot + 16 : (tile_bytes + 32 + 15) / 16 * 16;
   if (lds > fn::kTileBytesMax + 64) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");

@@ -528,8 +528,15 @@ struct Pad4Chunk {
   __device__ __forceinline__ void values(const uint8_t* s_tile, int32_t row_lds,
                                          const SampleParams& P, int32_t h, float (&v)[8]) const {
     const bool flip = kSrc != kSrcAny ? kSrc == kSrcFlip : P.flip != 0;
-    const int32_t b0 = row_lds + (flip ? mirror : direct);
-    const int32_t step = flip ? -C : C;
+    // the two source pixels are 2C contiguous bytes: w0, w0 + 1 unflipped,
+    // W-2-w0, W-1-w0 (output pixels 1, 0) flipped; read as three aligned
+    // dwords shifted into place
+    const int32_t b = row_lds + (flip ? mirror - C : direct);
+    const uint32_t* wp = reinterpret_cast<const uint32_t*>(s_tile + (b & ~3));
+    const uint32_t sh = (uint32_t)b & 3u;
+    const uint32_t w0w = wp[0], w1w = wp[1], w2w = wp[2];
+    const uint32_t d[2] = {__builtin_amdgcn_alignbyte(w1w, w0w, sh),
+                           __builtin_amdgcn_alignbyte(w2w, w1w, sh)};
     bool er[2] = {false, false};
     if (P.erase && h >= P.i && h < P.i + P.eh) {
       er[0] = w0 >= P.j && w0 < P.j + P.ew;
@@ -537,10 +544,12 @@ struct Pad4Chunk {
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
+      const int sp = flip ? 1 - p : p;  // source pixel of output pixel p
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (c < C) {
-          const float x = (float)s_tile[b0 + p * step + c];
+          const int j = sp * C + c;  // byte of the window
+          const float x = (float)((d[j >> 2] >> (8 * (j & 3))) & 0xFFu);
           v[4 * p + c] = er[p] ? 0.0f : normalize<kComp>(x, mul[c], mul_lo[c], nsub[c], nsub_lo[c]);
         } else {
           v[4 * p + c] = 0.0f;
@@ -906,7 +915,14 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
     int32_t h;
     tile_row_image(a, T, T.n_first, r, &slot, &h);
     const Setup cs(a, x0);
-    cs.values(s_lds, staged_row(a, T, head, row, r), s_params[slot], h, v);
+    const SampleParams P = s_params[slot];
+    // one read form per image: shifted dwords serve every alignment, so the
+    // lanes of a wavefront that spans two rows of different alignment do
+    // not split
+    if (P.flip)
+      cs.template values<kSrcFlip>(s_lds, staged_row(a, T, head, row, r), P, h, v);
+    else
+      cs.template values<kSrcBytes>(s_lds, staged_row(a, T, head, row, r), P, h, v);
     store_group<OutT, E, true>(out + e0, v);
   }
   if (all_elements) return;
