@@ -88,6 +88,11 @@ typedef struct {
  *   out_dev     N*H*W*OC elements of out_dtype in NHWC order, OC = C (no
  *               padding) or 4 for FN_OUT_FP16_PAD4, aligned to the element
  *               size (4 or 2 bytes); must not overlap the input.
+ *               Speed only: a 16-byte aligned out_dev whose rows are whole
+ *               16-byte vectors (W*OC*element size a multiple of 16) takes
+ *               the fastest kernel; other outputs take a flat layout at
+ *               about two thirds of its rate; input rows wider than 24,576
+ *               bytes take slower fallbacks.  Results are the same bits.
  *
  * Result, per sample n with P = fn_params(seed, ...)[n]:
  *   out[n,h,w,c] = +0                                 if P.erase and
