@@ -155,3 +155,23 @@ def test_inception_sized_batch(b):
     torch.cuda.synchronize()
     ref, _ = oracle.fused_normalize(x, mean, std, 0.5, 0.5, seed=123, threads=THREADS)
     check_values(out.cpu().numpy(), ref, "299x299", rne_exact=True)
+
+
+@pytest.mark.parametrize("out_dtype", [0, 1, 2])
+def test_flat_kernel_gives_the_tiles_kernel_bits(b, out_dtype):
+    """224-wide rows: the 16-byte aligned output takes the tiles kernel, the
+    same call with the output one, three and five elements past alignment
+    takes the flat kernel; all give the same bits, at random constants (the
+    two-fma form) and at the ImageNet constants (one fma)."""
+    shape = (4, 30, 224, 3)
+    x = np.random.default_rng(224).integers(0, 256, size=shape, dtype=np.uint8)
+    esz = 4 if out_dtype == 0 else 2
+    rng = np.random.default_rng(9)
+    for mean, std in (IMAGENET, (tuple(rng.uniform(0.3, 0.6, 3)), tuple(rng.uniform(0.2, 0.3, 3)))):
+        mean = tuple(float(v) for v in mean)
+        std = tuple(float(v) for v in std)
+        aligned = run_guarded(b, x, mean, std, 0.5, 1.0, 31, out_dtype, 0)
+        for k in (1, 3, 5):
+            say(f"flat vs tiles: out_dtype={out_dtype} offset={k * esz} bytes")
+            raw = run_guarded(b, x, mean, std, 0.5, 1.0, 31, out_dtype, k * esz)
+            assert np.array_equal(raw, aligned), f"offset {k * esz}: flat kernel bits differ"
