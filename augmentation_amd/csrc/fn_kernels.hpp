@@ -819,35 +819,39 @@ __device__ __forceinline__ float normalize_channel(const FusedArgs& a, float x, 
   return normalize<kComp>(x, m, ml, n, nl);
 }
 
-// Elements l0 .. l0 + E - 1 of a staged tile's outputs (l0 relative to the
-// tile's first output, count outputs in all), one at a time; elements
-// outside the tile are left 0.
+// Output l of a staged tile (l relative to the tile's first output).
+template <int C, int OC, bool kComp>
+__device__ __forceinline__ float flat_element(const FusedArgs& a, const Tile& T,
+                                              const uint8_t* s_lds, const SampleParams* s_params,
+                                              int32_t head, int32_t l) {
+  const int32_t row = a.W * C;
+  const int32_t row_out = a.W * OC;
+  const int32_t r = (int32_t)fast_div((uint32_t)l, a.div_row_out);
+  const int32_t x = l - r * row_out;
+  const int32_t w = x / OC;
+  const int32_t c = x - w * OC;
+  uint32_t slot;
+  int32_t h;
+  tile_row_image(a, T, T.n_first, r, &slot, &h);
+  const SampleParams P = s_params[slot];
+  const bool erased = P.erase && h >= P.i && h < P.i + P.eh && w >= P.j && w < P.j + P.ew;
+  if (c >= C || erased) return 0.0f;
+  const int32_t sw = P.flip ? a.W - 1 - w : w;
+  const float xb = (float)s_lds[staged_row(a, T, head, row, r) + sw * C + c];
+  return normalize_channel<C, kComp>(a, xb, c);
+}
+
+// Outputs l0 .. l0 + E - 1 of a staged tile, one at a time; those outside
+// the tile (count outputs) are left 0.
 template <int C, int OC, int E, bool kComp>
 __device__ __forceinline__ void flat_elements(const FusedArgs& a, const Tile& T,
                                               const uint8_t* s_lds, const SampleParams* s_params,
                                               int32_t head, int32_t l0, int32_t count,
                                               float (&v)[E]) {
-  const int32_t row = a.W * C;
-  const int32_t row_out = a.W * OC;
 #pragma unroll
   for (int k = 0; k < E; ++k) {
     const int32_t l = l0 + k;
-    v[k] = 0.0f;
-    if (l < 0 || l >= count) continue;
-    const int32_t r = (int32_t)fast_div((uint32_t)l, a.div_row_out);
-    const int32_t x = l - r * row_out;
-    const int32_t w = x / OC;
-    const int32_t c = x - w * OC;
-    uint32_t slot;
-    int32_t h;
-    tile_row_image(a, T, T.n_first, r, &slot, &h);
-    const SampleParams P = s_params[slot];
-    const bool erased = P.erase && h >= P.i && h < P.i + P.eh && w >= P.j && w < P.j + P.ew;
-    if (c < C && !erased) {
-      const int32_t sw = P.flip ? a.W - 1 - w : w;
-      const float xb = (float)s_lds[staged_row(a, T, head, row, r) + sw * C + c];
-      v[k] = normalize_channel<C, kComp>(a, xb, c);
-    }
+    v[k] = l >= 0 && l < count ? flat_element<C, OC, kComp>(a, T, s_lds, s_params, head, l) : 0.0f;
   }
 }
 
@@ -860,9 +864,9 @@ __device__ __forceinline__ void flat_elements(const FusedArgs& a, const Tile& T,
 // chunk, evaluated as in fused_tiles_kernel with its own lane setup; the
 // lanes take those first, one vector each in turn.  The other vectors hold
 // a row start (or the tile's end) at an element other than their first: a
-// second pass walks the tile's row starts, one per lane, and evaluates each
-// such vector element by element, so that the few of them do not hold up
-// whole wavefronts of the first pass.  Only the tile's own elements are
+// second pass walks the tile's row starts and gives each element of such a
+// vector a lane of its own, so that the few of them neither hold up whole
+// wavefronts of the first pass nor leave a few lanes working alone.  Only the tile's own elements are
 // stored: the tile next to it stores the rest of a vector they share, so no
 // byte is written twice.
 template <int C, typename OutT, bool kPad4, bool kComp>
@@ -928,9 +932,13 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
   if (all_elements) return;
 
   // second pass: the vector holding the start of row b (b = T.rows: the
-  // tile's end) when that is not its first element; a vector holding
-  // several row starts is done at the first of them
-  for (int32_t b = (int32_t)threadIdx.x; b <= T.rows; b += kThreads) {
+  // tile's end) when that is not its first element, one element per lane
+  // (E lanes per vector); a vector holding several row starts is done at
+  // the first of them
+  const int32_t n2 = (T.rows + 1) * E;
+  for (int32_t t = (int32_t)threadIdx.x; t < n2; t += kThreads) {
+    const int32_t b = t / E;
+    const int32_t k = t - b * E;
     const int64_t e = f0 + (int64_t)b * row_out + mu;  // shifted element index
     if (e % E == 0) continue;
     const int64_t kv = e / E;
@@ -939,16 +947,9 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
       if (ep % E != 0 && ep / E == kv) continue;
     }
     const int64_t e0 = kv * E - mu;
-    const int32_t l0 = (int32_t)(e0 - f0);
-    float v[E];
-    flat_elements<C, OC, E, kComp>(a, T, s_lds, s_params, head, l0, count, v);
-    if (l0 >= 0 && l0 + E <= count) {
-      store_group<OutT, E, true>(out + e0, v);
-    } else {
-#pragma unroll
-      for (int k = 0; k < E; ++k)
-        if (l0 + k >= 0 && l0 + k < count) out[e0 + k] = to_out<OutT>(v[k]);
-    }
+    const int32_t l = (int32_t)(e0 - f0) + k;
+    if (l < 0 || l >= count) continue;
+    out[e0 + k] = to_out<OutT>(flat_element<C, OC, kComp>(a, T, s_lds, s_params, head, l));
   }
 }
 
