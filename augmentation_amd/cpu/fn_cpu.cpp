@@ -16,7 +16,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <new>
 #include <string>
+#include <system_error>
 #include <thread>
 #include <vector>
 
@@ -274,6 +276,7 @@ struct Job {
   const Consts* k;
   const Gather* gather;
   fn_cpu_sample_params* params;  // may be null
+  uint8_t* rowbuf;               // one output row in output order, plus 32 bytes
 };
 
 void run_job(const Job& j) {
@@ -281,7 +284,6 @@ void run_job(const Job& j) {
   const int C = k.C, oc = k.oc;
   const int64_t in_row = (int64_t)j.W * C, out_row = (int64_t)j.W * oc;
   const int esz = k.out == FN_CPU_OUT_FP32 ? 4 : 2;
-  std::vector<uint8_t> rowbuf((size_t)out_row + 32);
   for (int64_t n = j.n_begin; n < j.n_end; ++n) {
     fn_cpu_sample_params P;
     draw_sample(*j.draw, j.seed, (uint64_t)(j.first_sample_id + n), &P);
@@ -292,8 +294,8 @@ void run_job(const Job& j) {
       const uint8_t* row = img + (int64_t)h * in_row;
       const uint8_t* src = row;
       if (P.flip || oc != C) {  // bytes in output order: mirrored pixels and/or padding
-        j.gather->row(row, j.W, P.flip != 0, rowbuf.data());
-        src = rowbuf.data();
+        j.gather->row(row, j.W, P.flip != 0, j.rowbuf);
+        src = j.rowbuf;
       }
       normalize_row(k, src, out_row, outb + (int64_t)h * out_row * esz);
     }
@@ -327,6 +329,7 @@ FNC_EXPORT int fn_cpu_fused_normalize(const uint8_t* in, int64_t N, int32_t H, i
       out_dtype != FN_CPU_OUT_FP16_PAD4)
     return fail(FN_CPU_EINVAL, "unknown out_dtype");
   if (first_sample_id < 0) return fail(FN_CPU_EINVAL, "first_sample_id must be >= 0");
+  if (N > INT64_MAX / 16 / ((int64_t)H * W)) return fail(FN_CPU_EINVAL, "N*H*W*16 overflows int64");
   if (N == 0) return 0;
   if (!in || !out || !mean || !std) return fail(FN_CPU_EINVAL, "NULL pointer");
   for (int c = 0; c < C; ++c)
@@ -367,16 +370,32 @@ FNC_EXPORT int fn_cpu_fused_normalize(const uint8_t* in, int64_t N, int32_t H, i
 
   const Gather gather(C, k.oc);
   const int T = (int)std::max<int64_t>(1, std::min<int64_t>(threads, N));
-  std::vector<Job> jobs(T);
-  for (int t = 0; t < T; ++t)
-    jobs[t] = Job{in,  out, N * t / T, N * (t + 1) / T, H, W, seed, first_sample_id, &d, &k,
-                  &gather, params};
-  if (T == 1) {
-    run_job(jobs[0]);
-  } else {
-    std::vector<std::thread> pool;
-    for (int t = 0; t < T; ++t) pool.emplace_back(run_job, std::cref(jobs[t]));
-    for (auto& th : pool) th.join();
+  // everything that can fail is obtained before any output is written
+  std::vector<Job> jobs;
+  std::vector<std::vector<uint8_t>> rowbufs;
+  std::vector<std::thread> pool;
+  try {
+    jobs.resize(T);
+    rowbufs.resize(T);
+    for (auto& b : rowbufs) b.resize((size_t)(W * (int64_t)k.oc) + 32);
+    pool.reserve(T);
+  } catch (const std::bad_alloc&) {
+    return fail(FN_CPU_ENOMEM, "out of host memory");
   }
+  for (int t = 0; t < T; ++t)
+    jobs[t] = Job{in, out, (int64_t)((__int128)N * t / T), (int64_t)((__int128)N * (t + 1) / T),
+                  H, W, seed, first_sample_id, &d, &k, &gather, params, rowbufs[t].data()};
+  int started = 0;
+  if (T > 1) {
+    for (; started < T; ++started) {
+      try {
+        pool.emplace_back(run_job, std::cref(jobs[started]));
+      } catch (const std::system_error&) {
+        break;  // no more threads: the calling thread does the rest
+      }
+    }
+  }
+  for (int t = started; t < T; ++t) run_job(jobs[t]);
+  for (auto& th : pool) th.join();
   return 0;
 }

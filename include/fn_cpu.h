@@ -35,6 +35,7 @@ extern "C" {
 #endif
 
 #define FN_CPU_EINVAL (-1)
+#define FN_CPU_ENOMEM (-2)  /* host memory for the per-thread row buffers */
 
 #define FN_CPU_OUT_FP32 0       /* 4-byte floats                                 */
 #define FN_CPU_OUT_FP16 1       /* 2-byte halves, C channels per pixel           */
@@ -59,8 +60,10 @@ typedef struct {
  *   params     NULL, or N records that receive each sample's decisions.
  *   threads    worker threads (images are split evenly); < 1 means 1.
  *
- * Synchronous; returns 0, or FN_CPU_EINVAL (message from fn_cpu_last_error()
- * on the calling thread) with nothing written.
+ * Synchronous; returns 0, or FN_CPU_EINVAL or FN_CPU_ENOMEM (message from
+ * fn_cpu_last_error() on the calling thread) with nothing written.  When the
+ * system refuses a worker thread, the calling thread processes that
+ * thread's images itself.
  */
 int fn_cpu_fused_normalize(const uint8_t* in, int64_t N, int32_t H, int32_t W, int32_t C,
                            const float* mean, const float* std, float flip_p, float erase_p,

@@ -184,3 +184,15 @@ def test_invalid_arguments_rejected(cs, kw):
         return
     with pytest.raises(cs.FnCpuError):
         cs.fused_normalize(x, out_dtype=od, **args)
+
+
+def test_batch_size_overflow_rejected(cs):
+    """N*H*W*16 beyond int64 is refused before anything is read or written."""
+    m = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
+    sd = (ctypes.c_float * 3)(0.25, 0.25, 0.25)
+    x = np.zeros(16, np.uint8)
+    out = np.zeros(16, np.float32)
+    rc = cs._lib.fn_cpu_fused_normalize(x.ctypes.data, 1 << 50, 4096, 4096, 3, m, sd, 0.5, 0.5,
+                                        0.02, 0.33, 0.3, 3.3, 1, 0, 0, out.ctypes.data, None, 4)
+    assert rc == -1 and b"overflow" in cs._lib.fn_cpu_last_error()
+    assert not out.any()
