@@ -13,11 +13,11 @@
 #include <immintrin.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
 #include <new>
-#include <string>
 #include <system_error>
 #include <thread>
 #include <vector>
@@ -28,10 +28,12 @@
 
 namespace {
 
-thread_local std::string g_error;
+// the last error message of this thread (a fixed buffer: recording an error
+// never allocates)
+thread_local char g_error[256];
 
 int fail(int code, const char* msg) {
-  g_error = msg;
+  snprintf(g_error, sizeof(g_error), "%s", msg);
   return code;
 }
 
@@ -309,7 +311,7 @@ void run_job(const Job& j) {
 
 }  // namespace
 
-FNC_EXPORT const char* fn_cpu_last_error(void) { return g_error.c_str(); }
+FNC_EXPORT const char* fn_cpu_last_error(void) { return g_error; }
 
 FNC_EXPORT int fn_cpu_fused_normalize(const uint8_t* in, int64_t N, int32_t H, int32_t W,
                                       int32_t C, const float* mean, const float* std, float flip_p,
@@ -317,7 +319,7 @@ FNC_EXPORT int fn_cpu_fused_normalize(const uint8_t* in, int64_t N, int32_t H, i
                                       float ratio_min, float ratio_max, uint64_t seed,
                                       int64_t first_sample_id, int32_t out_dtype, void* out,
                                       fn_cpu_sample_params* params, int32_t threads) {
-  g_error.clear();
+  g_error[0] = '\0';
   if (H <= 0 || W <= 0 || C < 1 || C > 4 || N < 0) return fail(FN_CPU_EINVAL, "bad shape");
   if ((int64_t)H * W > ((int64_t)1 << 24)) return fail(FN_CPU_EINVAL, "H*W exceeds 2^24");
   if (!(flip_p >= 0.0f && flip_p <= 1.0f) || !(erase_p >= 0.0f && erase_p <= 1.0f))

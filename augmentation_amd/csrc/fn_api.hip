@@ -9,7 +9,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <string>
 
 #include "fn.h"
 #include "fn_kernels.hpp"
@@ -19,20 +18,20 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// the last error message of this thread: a fixed buffer, so that recording
+// an error never allocates (and nothing can throw across the C ABI)
+thread_local char g_last_error[512];
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return code;
 }
 
 int ok() {
-  g_last_error.clear();
+  g_last_error[0] = '\0';
   return FN_OK;
 }
 
@@ -410,7 +409,7 @@ void launch_grouped(const fn::FusedArgs& a, int C, int px, int out_dtype, unsign
 
 }  // namespace
 
-FN_EXPORT const char* fn_last_error(void) { return g_last_error.c_str(); }
+FN_EXPORT const char* fn_last_error(void) { return g_last_error; }
 
 FN_EXPORT int fn_params_ex(uint64_t seed, int64_t first_sample_id, int64_t N, int32_t H,
                            int32_t W, float flip_p, float erase_p, float scale_min,
