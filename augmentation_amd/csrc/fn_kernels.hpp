@@ -858,17 +858,17 @@ __device__ __forceinline__ void flat_elements(const FusedArgs& a, const Tile& T,
 // The fused pass for outputs that the lane layout of fused_tiles_kernel does
 // not fit: rows of W*OC outputs that are not a whole number of 16-byte
 // vectors, or an output aligned only to its element size.  The tile is
-// staged as there.  Its outputs are the contiguous elements [F0, F1) of the
-// output, covered by the 16-byte-aligned vectors of the output buffer.
-// A vector inside one row (and, when kPad4, starting at a pixel) is one
-// chunk, evaluated as in fused_tiles_kernel with its own lane setup; the
-// lanes take those first, one vector each in turn.  The other vectors hold
-// a row start (or the tile's end) at an element other than their first: a
-// second pass walks the tile's row starts and gives each element of such a
-// vector a lane of its own, so that the few of them neither hold up whole
-// wavefronts of the first pass nor leave a few lanes working alone.  Only the tile's own elements are
-// stored: the tile next to it stores the rest of a vector they share, so no
-// byte is written twice.
+// staged as there.  Its outputs are the count contiguous elements from f0 on,
+// covered by the 16-byte-aligned vectors of the output buffer.  A vector
+// inside one row (and, when kPad4, starting at a pixel) is one chunk,
+// evaluated as in fused_tiles_kernel with its own lane setup; the lanes take
+// those first, one vector each in turn.  The other vectors hold a row start
+// (or the tile's end) at an element other than their first: a second pass
+// walks the tile's row starts and gives each element of such a vector a lane
+// of its own, so that the few of them neither hold up whole wavefronts of the
+// first pass nor leave a few lanes working alone.  Only the tile's own
+// elements are stored: the tile next to it stores the rest of a vector they
+// share, so no byte is written twice.
 template <int C, typename OutT, bool kPad4, bool kComp>
 __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(FusedArgs a) {
   constexpr int kThreads = tiles_threads<OutT>();
