@@ -175,3 +175,41 @@ def test_flat_kernel_gives_the_tiles_kernel_bits(b, out_dtype):
             say(f"flat vs tiles: out_dtype={out_dtype} offset={k * esz} bytes")
             raw = run_guarded(b, x, mean, std, 0.5, 1.0, 31, out_dtype, k * esz)
             assert np.array_equal(raw, aligned), f"offset {k * esz}: flat kernel bits differ"
+
+
+def test_flat_kernel_beyond_4gib(b):
+    """28,700 images of 224x224x3 (more than 2^32 input bytes, 8.6 GB of fp16
+    output) written once 16-byte aligned (tiles kernel) and once 2 bytes past
+    that (flat kernel): the two outputs are the same bits over the whole
+    batch, and the images on both sides of the 4 GiB input boundary, the
+    first and the last equal RNE16(oracle) -- 32-bit offset arithmetic in
+    the flat kernel would show here.  The input is drawn on the GPU from a
+    seeded generator."""
+    N, H, W, C = 28700, 224, 224, 3
+    img = H * W * C
+    assert N * img > 2**32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4243)
+    say(f"flat beyond 4 GiB: {N} images")
+    x = torch.randint(0, 256, (N, H, W, C), dtype=torch.uint8, device="cuda", generator=g)
+    mean, std = IMAGENET
+    args = (N, H, W, C, mean, std, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, 777, 1)
+    aligned = torch.empty((N, H, W, C), dtype=torch.float16, device="cuda")
+    b.fn_fused_normalize(x, *args, aligned)
+    buf = torch.empty(N * img * 2 + 16, dtype=torch.uint8, device="cuda")
+    b.fn_fused_normalize(x, *args, buf.data_ptr() + 2)
+    torch.cuda.synchronize()
+    shifted = buf[2:2 + N * img * 2].view(torch.int16).view(N, H, W, C)
+    same = all(torch.equal(aligned[i:i + 2048].view(torch.int16), shifted[i:i + 2048])
+               for i in range(0, N, 2048))
+    assert same, "flat kernel bits differ from the tiles kernel's"
+    boundary = 2**32 // img
+    picks = [0, boundary - 1, boundary, boundary + 1, N - 1]
+    idx = torch.tensor(picks, device="cuda")
+    xs = x.index_select(0, idx).cpu().numpy()
+    got = shifted.index_select(0, idx).cpu().numpy().view(np.float16)
+    del x, aligned, buf, shifted
+    torch.cuda.empty_cache()
+    for k, n in enumerate(picks):
+        ref, _ = oracle.fused_normalize(xs[k:k + 1], mean, std, 0.5, 0.5, seed=777, first_n=n)
+        check_values(got[k:k + 1], ref, f"flat beyond 4 GiB, image {n}")
