@@ -213,3 +213,32 @@ def test_flat_kernel_beyond_4gib(b):
     for k, n in enumerate(picks):
         ref, _ = oracle.fused_normalize(xs[k:k + 1], mean, std, 0.5, 0.5, seed=777, first_n=n)
         check_values(got[k:k + 1], ref, f"flat beyond 4 GiB, image {n}")
+
+
+def test_flat_kernel_graph_capture_replays_match_eager(b):
+    """The flat kernel, like the tiles kernel, allocates nothing and issues
+    no memset: a captured call (299-wide rows, fp16) replayed five times,
+    with eager work between replays, each equal to the eager call."""
+    shape = (64, 40, 299, 3)
+    N, H, W, C = shape
+    xt = torch.from_numpy(np.random.default_rng(31).integers(0, 256, size=shape, dtype=np.uint8)).cuda()
+    mean, std = IMAGENET
+    args = (N, H, W, C, mean, std, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, 55, 1)
+    eager = torch.empty(shape, dtype=torch.float16, device="cuda")
+    b.fn_fused_normalize(xt, *args, eager)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        b.fn_fused_normalize(xt, *args, out, s)
+    torch.cuda.synchronize()
+    for k in range(5):
+        say(f"flat graph replay {k}")
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), k
+        _ = (xt.float() * 2).sum().item()  # unrelated eager work between replays
