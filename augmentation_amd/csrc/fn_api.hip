@@ -156,6 +156,40 @@ size_t device_lds_per_cu(int dev) {
   return v > 0 ? (size_t)v : 0;
 }
 
+// LDS bytes one work-group may use on device `dev`, cached per device; 0 if
+// the runtime does not report it.
+size_t device_lds_per_block(int dev) {
+  static std::atomic<long> cache[64];
+  if (dev >= 0 && dev < 64) {
+    const long c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c > 0 ? (size_t)c : 0;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    v = 0;
+  }
+  if (dev >= 0 && dev < 64) cache[dev].store(v > 0 ? (long)v : -1, std::memory_order_relaxed);
+  return v > 0 ? (size_t)v : 0;
+}
+
+// Largest staging buffer of a tiles-kernel work-group on device `dev`: what
+// one work-group may hold (all: true), or what lets two share a compute unit
+// (all: false), after the decision records and a margin.  Rows up to the
+// second take the tiles kernels outright (measured: they beat the pixel-group
+// kernel there); wider rows up to the first take them when the pixel-group
+// kernel does not apply (one resident work-group per compute unit still beats
+// the element-wise kernel).
+int64_t tile_buffer_limit(int dev, bool all) {
+  const int64_t fixed = (int64_t)sizeof(fn::SampleParams) * fn::kMaxImagesPerBlock + 64;
+  // 64 KB per work-group and per compute unit where the runtime reports
+  // nothing (every CDNA device has at least that)
+  const int64_t block = device_lds_per_block(dev) > 0 ? (int64_t)device_lds_per_block(dev) : 65536;
+  const int64_t cu = device_lds_per_cu(dev) > 0 ? (int64_t)device_lds_per_cu(dev) : 65536;
+  const int64_t lim = all ? block : std::min(block, cu / 2);
+  return std::max<int64_t>(lim - fixed, 0);
+}
+
 // Dynamic LDS of one tiles-kernel work-group: its staging buffer, padded so
 // that at most kWgsPerCu work-groups fit on a compute unit (fewer resident
 // work-groups queue less at the memory and finish sooner; measured).  The
@@ -360,7 +394,7 @@ bool single_fma_exact(const fn::FusedArgs& a, int C, int out_dtype) {
 // tiles.  row_slot > 0: strided rows, staged row_slot LDS bytes apart.
 // Sets the tile fields of `a`.
 int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elems, int cus,
-               int64_t row_slot) {
+               int64_t row_slot, int64_t lds_limit) {
   // LDS bytes one row occupies: the row itself, or its slot of whole
   // granules when strided (never fewer than 32 bytes, however narrow the row)
   const int64_t row_lds = row_slot > 0 ? row_slot : row;
@@ -391,7 +425,7 @@ int plan_tiles(fn::FusedArgs* a, int64_t N, int32_t H, int64_t row, int64_t elem
   // contiguous layout's 32 extra bytes cover them too)
   const int64_t tile_rows = a->images_per_tile == 1 ? a->rows_per_tile : a->images_per_tile * H;
   const int64_t lds = row_slot > 0 ? tile_rows * row_slot + 16 : (tile_bytes + 32 + 15) / 16 * 16;
-  if (lds > fn::kTileBytesMax + 64) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
+  if (lds > lds_limit) return fail(FN_EOVERFLOW, "tile exceeds the LDS budget");
   if (a->total_tiles > 0x7FFFFFFF) return fail(FN_EOVERFLOW, "grid size limit exceeded");
   a->lds_buffer_bytes = (int32_t)lds;
   return FN_OK;
@@ -537,13 +571,19 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
   a.in_image_stride = image_stride;
   a.strided = strided ? 1 : 0;
   const int64_t row_out = (int64_t)W * oc;
-  if (row <= fn::kTileBytesMax) {
+  // strided rows: one slot of whole 16-byte granules per row
+  const int64_t row_slot = strided ? (15 + row + 15) / 16 * 16 : 0;
+  // the staging buffer of a one-row tile (plan_tiles' sizes)
+  const int64_t one_row = strided ? row_slot + 16 : (row + 32 + 15) / 16 * 16;
+  const int px = out_dtype == FN_OUT_FP16_PAD4 || strided
+                     ? 0
+                     : pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);
+  const int64_t lds_all = tile_buffer_limit(dev, true);
+  if (one_row <= tile_buffer_limit(dev, false) || (px == 0 && one_row <= lds_all)) {
     int cus = 0;
     rc = device_cu_count(dev, &cus);
     if (rc) return rc;
-    // strided rows: one slot of whole 16-byte granules per row
-    const int64_t row_slot = strided ? (15 + row + 15) / 16 * 16 : 0;
-    rc = plan_tiles(&a, N, H, row, elems, cus, row_slot);
+    rc = plan_tiles(&a, N, H, row, elems, cus, row_slot, lds_all);
     if (rc) return rc;
     a.row_slot = (int32_t)row_slot;
     a.div_gps = make_fast_div((uint32_t)std::max<int64_t>(row_slot / 16, 1));
@@ -573,9 +613,6 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
     launch_flat(a, C, out_dtype, comp, (unsigned)a.total_tiles, lds, st);
     return launch_status("fused_flat_kernel launch");
   }
-  const int px = out_dtype == FN_OUT_FP16_PAD4 || strided
-                     ? 0
-                     : pick_group_pixels(W, C, out_bytes, (uintptr_t)in_u8_dev, (uintptr_t)out_dev);
   if (px > 0) {
     a.groups_per_row = (uint32_t)(W / px);
     a.groups_per_image = (uint32_t)((int64_t)H * W / px);

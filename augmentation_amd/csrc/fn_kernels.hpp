@@ -15,14 +15,15 @@
 //                          lanes take the buffer's aligned 16-byte vectors,
 //                          and the few that hold a row start are done element
 //                          by element in a second pass.
-//   fused_grouped_kernel   rows too wide for a tile, when the width is a
-//                          multiple of a pixel group PX and the output is
-//                          16-byte aligned: each lane owns groups of PX
-//                          consecutive pixels of one row; a flipped group
-//                          reads the mirrored group of the same row and
-//                          reverses the pixel order in registers, keeping the
-//                          channel order; a group wholly inside the erase
-//                          rectangle reads nothing.
+//   fused_grouped_kernel   rows whose one-row tile would leave room for only
+//                          one work-group per compute unit (or not fit at
+//                          all), when the width is a multiple of a pixel
+//                          group PX and the output is 16-byte aligned: each
+//                          lane owns groups of PX consecutive pixels of one
+//                          row; a flipped group reads the mirrored group of
+//                          the same row and reverses the pixel order in
+//                          registers, keeping the channel order; a group
+//                          wholly inside the erase rectangle reads nothing.
 //   fused_generic_kernel   any other row too wide for a tile, one element at
 //                          a time.
 //   Values are (x/255 - mean)/std from fp32 constant pairs (see
@@ -77,7 +78,6 @@ constexpr int kBlock = 256;             // four wave64 wavefronts
 constexpr int kTileBytesTarget = FN_TILE_BYTES;
 constexpr int kMinTileBytes = FN_MIN_TILE_BYTES;
 constexpr int kWgsPerCu = FN_WGS_PER_CU;
-constexpr int kTileBytesMax = 24576;    // largest tile (one row at least) staged in LDS
 constexpr int kMaxImagesPerBlock = 16;  // images whose decisions one work-group draws
 constexpr int kMaxIter = FN_GROUP_ITER;  // pixel groups per lane in the grouped kernel
 constexpr int kGroupPxMax = FN_GROUP_PX_MAX;

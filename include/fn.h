@@ -91,8 +91,9 @@ typedef struct {
  *               Speed only: a 16-byte aligned out_dev whose rows are whole
  *               16-byte vectors (W*OC*element size a multiple of 16) takes
  *               the fastest kernel; other outputs take a flat layout at
- *               about two thirds of its rate; input rows wider than 24,576
- *               bytes take slower fallbacks.  Results are the same bits.
+ *               about two thirds of its rate; input rows that leave room
+ *               for only one tile per compute unit in LDS (about 80 KB on
+ *               MI355X) take slower paths.  Results are the same bits.
  *
  * Result, per sample n with P = fn_params(seed, ...)[n]:
  *   out[n,h,w,c] = +0                                 if P.erase and

@@ -242,3 +242,46 @@ def test_flat_kernel_graph_capture_replays_match_eager(b):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), k
         _ = (xt.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+# Rows wider than the usual tiles, each shape aimed at one route through the
+# library (comments: the kernel the host picks on a device with 160 KB of LDS
+# per work-group and per compute unit).
+WIDE = [
+    ((1, 3, 12000, 3), 1, 0),   # one-row tiles of 36 KB: tiles kernel
+    ((1, 3, 12001, 3), 1, 2),   # one-row tiles, rows inside vectors: flat kernel
+    ((1, 2, 28000, 3), 1, 0),   # 84 KB rows, W a multiple of 16, aligned: pixel-group kernel
+    ((1, 2, 28000, 3), 1, 2),   # the same rows, output off alignment: flat, one work-group per CU
+    ((1, 2, 28001, 3), 0, 0),   # 84 KB rows, odd width, fp32: flat, one work-group per CU
+    ((1, 2, 28001, 3), 2, 0),   # the same, padded layout
+    ((1, 2, 56000, 3), 1, 0),   # 168 KB rows (beyond LDS), aligned: pixel-group kernel
+    ((1, 2, 56001, 3), 1, 0),   # 168 KB rows, odd width: element-wise kernel
+]
+
+
+@pytest.mark.parametrize("case", WIDE)
+def test_wide_rows(b, case):
+    shape, out_dtype, out_off = case
+    N, H, W, C = shape
+    x = np.random.default_rng(W).integers(0, 256, size=shape, dtype=np.uint8)
+    mean, std = IMAGENET
+    seed = 600 + W
+    ref, _ = oracle.fused_normalize(x, mean, std, 0.5, 1.0, seed=seed)
+    say(f"wide rows: {shape} out_dtype={out_dtype} out_off={out_off}")
+    raw = run_guarded(b, x, mean, std, 0.5, 1.0, seed, out_dtype, out_off)
+    check(as_values(raw, shape, out_dtype), ref, C, out_dtype, f"wide {shape}", True)
+
+
+def test_wide_strided_window(b):
+    """A 30,000-pixel window (90 KB rows) read through row and image strides
+    (one-row tiles with strided loads), odd offset into the source."""
+    src = np.random.default_rng(30000).integers(0, 256, size=(2, 3, 30011, 3), dtype=np.uint8)
+    y0, x0, H, W = 1, 5, 2, 30000
+    win = np.ascontiguousarray(src[:, y0:y0 + H, x0:x0 + W, :])
+    mean, std = IMAGENET
+    ref, _ = oracle.fused_normalize(win, mean, std, 0.5, 1.0, seed=8, first_n=3)
+    say("wide strided window")
+    raw = run_guarded(b, src, mean, std, 0.5, 1.0, 8, 1, 0,
+                      strides=(30011 * 3, 3 * 30011 * 3, (y0 * 30011 + x0) * 3, (2, H, W, 3)),
+                      first_sample_id=3)
+    check(as_values(raw, (2, H, W, 3), 1), ref, 3, 1, "wide strided", True)

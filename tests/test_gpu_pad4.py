@@ -61,7 +61,7 @@ PAD4_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1,
                (1, 1, 17, 3), (5, 17, 1, 3), (3, 2, 2, 1), (2, 31, 33, 3), (7, 13, 12, 4),
                (2, 4, 4096, 1), (1, 600, 6, 3), (9, 28, 28, 1), (64, 32, 32, 3),
                (2, 3, 1024, 3), (2, 5, 700, 2), (40, 8, 8, 2), (3, 64, 48, 3),
-               (1, 3, 9000, 3)]  # a row wider than the largest LDS tile
+               (1, 3, 9000, 3)]  # a 27 KB row: one-row tiles
 
 
 @pytest.mark.parametrize("shape", PAD4_SHAPES)

@@ -179,11 +179,11 @@ EDGE_SHAPES = [(3, 5, 7, 1), (2, 9, 5, 2), (4, 6, 5, 3), (2, 3, 3, 4), (1, 1, 1,
                (1, 1, 17, 3), (5, 17, 1, 3), (3, 2, 2, 1), (2, 31, 33, 3), (7, 13, 11, 4),
                (2, 4, 8192, 1), (1, 600, 6, 3), (9, 28, 28, 1), (64, 32, 32, 3),
                (2, 3, 1024, 3), (2, 5, 700, 4), (40, 8, 8, 2), (3, 64, 48, 3),
-               # rows wider than the largest LDS tile (24 KB): the pixel-group
-               # kernel (W a multiple of 8, aligned output) and the element-wise
-               # one; the other shapes take the tiles kernel or, when a row ends
-               # inside a 16-byte vector or the output is only element aligned,
-               # the flat one
+               # wide rows (27 KB) in one-row tiles; the input offsets below keep
+               # the pixel-group kernel out, so every shape takes the tiles
+               # kernel or, when a row ends inside a 16-byte vector or the
+               # output is only element aligned, the flat one (the wide-row
+               # routes are in test_gpu_flat.py)
                (1, 3, 9000, 3), (1, 2, 9001, 3)]
 
 
