@@ -787,6 +787,38 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
         }
       }
     }
+  } else if (single) {
+    // Rows wider than one pass of the lanes: lane ct takes the chunk columns
+    // ct, ct + kThreads, ... and each column down all rows of the tile, so
+    // one lane setup serves the whole column; the decisions sit in scalar
+    // registers and the source read form is picked once, as above.
+    SampleParams P;
+    P.flip = __builtin_amdgcn_readfirstlane(P0.flip);
+    P.erase = __builtin_amdgcn_readfirstlane(P0.erase);
+    P.i = __builtin_amdgcn_readfirstlane(P0.i);
+    P.j = __builtin_amdgcn_readfirstlane(P0.j);
+    P.eh = __builtin_amdgcn_readfirstlane(P0.eh);
+    P.ew = __builtin_amdgcn_readfirstlane(P0.ew);
+    auto columns = [&](auto mode) {
+      constexpr int kSrc = decltype(mode)::value;
+      for (int32_t c = ct; c < cpr; c += kThreads) {
+        const Setup cs(a, c * E);
+        for (int32_t r = 0; r < T.rows; ++r) {
+          float v[E];
+          cs.template values<kSrc>(s_lds, row_lds(r), P, T.h0 + r, v);
+          store_group<OutT, E, true>(out + (int64_t)r * row_out + cs.x0, v);
+        }
+      }
+    };
+    const bool aligned = !a.strided && ((head | row) & 3) == 0;
+    if (P.flip)
+      columns(std::integral_constant<int, kSrcFlip>());
+    else if (a.strided)
+      columns(std::integral_constant<int, kSrcAny>());
+    else if (aligned)
+      columns(std::integral_constant<int, kSrcAligned>());
+    else
+      columns(std::integral_constant<int, kSrcBytes>());
   } else {
     const int32_t nchunks = T.rows * cpr;
     for (int32_t q = ct; q < nchunks; q += kThreads) {
@@ -796,7 +828,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       uint32_t slot;
       int32_t h;
       tile_row_image(a, T, T.n_first, (int32_t)r, &slot, &h);
-      const SampleParams P = single ? P0 : s_params[slot];
+      const SampleParams P = s_params[slot];
       const Setup cq(a, x0);
       float v[E];
       cq.values(s_lds, row_lds((int32_t)r), P, h, v);
