@@ -84,6 +84,7 @@ def counter_traffic() -> dict | None:
 
 
 OUT_NAMES = {0: "fp32", 1: "fp16", 2: "fp16, 4 channels per pixel"}
+OUT_CODES = {"fp32": 0, "fp16": 1, "fp16_pad4": 2}
 
 
 def describe(w) -> str:
@@ -163,13 +164,22 @@ def median_call_ms(launch, calls: int, sets: int, stream) -> float:
     return times[len(times) // 2]
 
 
-def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -> dict:
+def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float,
+                   out_offset: int = 0) -> dict:
+    """Time workload w (rotating `sets` buffer sets).  out_offset > 0 puts
+    each output that many bytes past a 16-byte boundary."""
     import torch
     stream = torch.cuda.current_stream()
     x = torch.from_numpy(w.make_input()).cuda()
     tdt = torch.float32 if w.out_dtype == 0 else torch.float16
     ins = [x] + [x.clone() for _ in range(sets - 1)]
-    outs = [torch.empty(w.out_shape, dtype=tdt, device="cuda") for _ in range(sets)]
+    if out_offset:
+        out_bytes = w.N * w.H * w.W * w.out_channels * w.out_bytes
+        bufs = [torch.empty(out_bytes + 16, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+        outs = [t.data_ptr() + out_offset for t in bufs]
+    else:
+        bufs = None
+        outs = [torch.empty(w.out_shape, dtype=tdt, device="cuda") for _ in range(sets)]
     torch.cuda.synchronize()
     seeds = w.seeds
 
@@ -191,7 +201,7 @@ def bench_workload(b, w, steps: int, warmup: int, sets: int, prewarm_s: float) -
     host = []
     ms = time_launches(launch, steps, warmup, sets, stream, prewarm_s, host)
     med = median_call_ms(launch, min(steps, 200), sets, stream)
-    del ins, outs
+    del ins, outs, bufs
     torch.cuda.empty_cache()
     return {"ms": ms, "median_call_ms": med, "host_ms": host[0], "images_per_s": w.N / (ms * 1e-3),
             "gbs": w.nominal_bytes / (ms * 1e-3) / 1e9}
@@ -359,6 +369,14 @@ def main() -> int:
     ap.add_argument("--workload", default=None,
                     help="time this workload instead of the headline one (the JSON line then "
                          "describes it; the metric line of record is the default)")
+    ap.add_argument("--shape", default=None, metavar="N,H,W,C",
+                    help="time a synthetic batch of this shape instead (uniform bytes, flip and "
+                         "erase 0.5, ImageNet constants for C = 3)")
+    ap.add_argument("--out", default="fp16", choices=sorted(OUT_CODES),
+                    help="output type for --shape")
+    ap.add_argument("--out-offset", type=int, default=0, metavar="BYTES",
+                    help="for --shape: put the output this many bytes past a 16-byte boundary "
+                         "(a multiple of the element size)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -378,12 +396,33 @@ def main() -> int:
         sweep(b, args.steps, args.warmup, args.prewarm_seconds,
               [int(v) for v in args.sweep.split(",")])
         return 0
-    name = args.workload or synth.HEADLINE
-    if name not in synth.WORKLOADS:
-        print(f"unknown workload {name!r}; known: {', '.join(synth.WORKLOADS)}", file=sys.stderr)
-        return 2
-    w = synth.WORKLOADS[name]
-    r = bench_workload(b, w, args.steps, args.warmup, args.sets, args.prewarm_seconds)
+    if args.shape:
+        try:
+            N, H, W, C = (int(v) for v in args.shape.split(","))
+        except ValueError:
+            print("--shape takes N,H,W,C", file=sys.stderr)
+            return 2
+        out_dtype = OUT_CODES[args.out]
+        esz = 4 if out_dtype == 0 else 2
+        if args.out_offset < 0 or args.out_offset % esz or args.out_offset >= 16:
+            print("--out-offset must be a multiple of the element size below 16", file=sys.stderr)
+            return 2
+        mean, std = ((synth.IMAGENET_MEAN, synth.IMAGENET_STD) if C == 3
+                     else ((0.5,) * C, (0.25,) * C))
+        name = f"shape {N}x{H}x{W}x{C} -> {args.out}" + (
+            f", output {args.out_offset} bytes past 16-byte alignment" if args.out_offset else "")
+        w = synth.Workload(name, N, H, W, C, mean, std, 0.5, 0.5, out_dtype, 1100)
+        sets = max(2, min(args.sets, -(-1_200_000_000 // w.nominal_bytes) + 1))
+    else:
+        name = args.workload or synth.HEADLINE
+        if name not in synth.WORKLOADS:
+            print(f"unknown workload {name!r}; known: {', '.join(synth.WORKLOADS)}",
+                  file=sys.stderr)
+            return 2
+        w = synth.WORKLOADS[name]
+        sets = args.sets
+    r = bench_workload(b, w, args.steps, args.warmup, sets, args.prewarm_seconds,
+                       args.out_offset if args.shape else 0)
     achieved = r["gbs"]
     traffic = counter_traffic() if name == synth.HEADLINE else None
 
@@ -403,7 +442,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": describe(w),
                    "N": w.N, "H": w.H, "W": w.W, "C": w.C, "out": OUT_NAMES[w.out_dtype],
-                   "rotating_sets": args.sets},
+                   "rotating_sets": sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),
