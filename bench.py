@@ -429,6 +429,19 @@ def main() -> int:
         print("bench.py measures one GPU only: the operation has no cross-GPU step and this "
               "build runs on a single MI355X (run with --gpus 1).", file=sys.stderr)
         return 2
+    shape = None
+    if args.shape:
+        try:
+            shape = tuple(int(v) for v in args.shape.split(","))
+        except ValueError:
+            shape = ()
+        if len(shape) != 4 or min(shape) < 1:
+            print("--shape takes N,H,W,C (positive integers)", file=sys.stderr)
+            return 2
+        esz = 4 if OUT_CODES[args.out] == 0 else 2
+        if args.out_offset < 0 or args.out_offset % esz or args.out_offset >= 16:
+            print("--out-offset must be a multiple of the element size below 16", file=sys.stderr)
+            return 2
 
     import torch
     from augmentation_amd import binding as b
@@ -442,17 +455,9 @@ def main() -> int:
         sweep(b, args.steps, args.warmup, args.prewarm_seconds,
               [int(v) for v in args.sweep.split(",")])
         return 0
-    if args.shape:
-        try:
-            N, H, W, C = (int(v) for v in args.shape.split(","))
-        except ValueError:
-            print("--shape takes N,H,W,C", file=sys.stderr)
-            return 2
+    if shape:
+        N, H, W, C = shape
         out_dtype = OUT_CODES[args.out]
-        esz = 4 if out_dtype == 0 else 2
-        if args.out_offset < 0 or args.out_offset % esz or args.out_offset >= 16:
-            print("--out-offset must be a multiple of the element size below 16", file=sys.stderr)
-            return 2
         mean, std = ((synth.IMAGENET_MEAN, synth.IMAGENET_STD) if C == 3
                      else ((0.5,) * C, (0.25,) * C))
         name = f"shape {N}x{H}x{W}x{C} -> {args.out}" + (
