@@ -83,3 +83,39 @@ def test_random_case(b, k):
     ref, _ = oracle.fused_normalize(x, c["mean"], c["std"], c["flip_p"], c["erase_p"],
                                     seed=c["seed"], first_n=c["first"])
     check(as_values(raw, (N, H, W, C), c["out_dtype"]), ref, C, c["out_dtype"], f"case {k}", False)
+
+
+WIDE_CASES = 30
+
+
+@pytest.mark.parametrize("k", range(WIDE_CASES))
+def test_random_wide_case(b, k):
+    """Rows of 3,000 to 40,000 pixels: one-row tiles up to the LDS limit, the
+    pixel-group kernel and the element-wise one, with the same random
+    offsets, strides and constants."""
+    c = make_case(10_000 + k)
+    rng = c["rng"]
+    c["W"] = int(np.exp(rng.uniform(np.log(3000), np.log(40000))))
+    c["H"] = int(rng.integers(1, 5))
+    c["N"] = int(rng.integers(1, 4))
+    c["strided"] = c["strided"] and c["W"] * c["C"] < 150_000
+    k_orig = k
+    N, H, W, C = c["N"], c["H"], c["W"], c["C"]
+    say(f"random wide case {k_orig}: N={N} H={H} W={W} C={C} out={c['out_dtype']} "
+        f"off={c['out_off']} strided={c['strided']}")
+    if c["strided"]:
+        sw = W + int(rng.integers(0, 9))
+        x0 = int(rng.integers(0, sw - W + 1))
+        src = rng.integers(0, 256, size=(N, H, sw, C), dtype=np.uint8)
+        x = np.ascontiguousarray(src[:, :, x0:x0 + W, :])
+        raw = run_guarded(b, src, c["mean"], c["std"], c["flip_p"], c["erase_p"], c["seed"],
+                          c["out_dtype"], c["out_off"], strides=(sw * C, H * sw * C, x0 * C, (N, H, W, C)),
+                          first_sample_id=c["first"])
+    else:
+        x = rng.integers(0, 256, size=(N, H, W, C), dtype=np.uint8)
+        raw = run_guarded(b, x, c["mean"], c["std"], c["flip_p"], c["erase_p"], c["seed"],
+                          c["out_dtype"], c["out_off"], strides=(W * C, H * W * C, 0, (N, H, W, C)),
+                          first_sample_id=c["first"])
+    ref, _ = oracle.fused_normalize(x, c["mean"], c["std"], c["flip_p"], c["erase_p"],
+                                    seed=c["seed"], first_n=c["first"])
+    check(as_values(raw, (N, H, W, C), c["out_dtype"]), ref, C, c["out_dtype"], f"wide case {k}", False)
