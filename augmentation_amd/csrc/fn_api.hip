@@ -192,8 +192,8 @@ int64_t tile_buffer_limit(int dev, bool all) {
 
 // Dynamic LDS of one tiles-kernel work-group: its staging buffer, padded so
 // that at most kWgsPerCu work-groups fit on a compute unit (fewer resident
-// work-groups queue less at the memory and finish sooner; measured).  The
-// padding never exceeds the 64 KB a work-group may request.
+// work-groups queue less at the memory and finish sooner; measured).  Only
+// buffers below that share are padded, and never beyond 64 KB.
 size_t tiles_lds_bytes(int dev, int32_t buffer_bytes) {
   size_t lds = (size_t)buffer_bytes;
   const size_t per_cu = device_lds_per_cu(dev);
