@@ -46,8 +46,8 @@ namespace fn {
 //   FN_GROUP_PX_MAX  widest pixel group tried (16, 8 or 4)
 //   FN_GROUP_ITER    pixel groups per lane (1..4)
 // and of the tiles kernel's lane-contiguous stores:
-//   FN_NT_STORE      0 default, 1 non-temporal, 2 streaming system-scope
-//                    (sc0 sc1 nt)
+//   FN_NT_STORE      policy of its 16-byte stores: 0 default, 1
+//                    non-temporal, 2 streaming system-scope (sc0 sc1 nt)
 #ifndef FN_GROUP_PX_MAX
 #define FN_GROUP_PX_MAX 16
 #endif
@@ -227,11 +227,19 @@ __device__ __forceinline__ void stream_store16(u32x4* p, u32x4 q) {
   asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" ::"v"(p), "v"(q) : "memory");
 }
 
-// Stores NE output values as 16-, 8- or 4-byte vectors.
-// kStream: 16-byte vectors with the streaming policy FN_NT_STORE (for
-// lane-contiguous stores); otherwise plain stores (lane-strided patterns,
-// where non-temporal stores measured 3x slower).
-template <typename OutT, int NE, bool kStream = false>
+// Cache policy of a 16-byte output store.  kStoreSys (sc0 sc1 nt) writes
+// through to memory at system scope: fastest where every 128-byte line is
+// written whole by one store instruction (the tiles kernel).  kStoreNt
+// leaves lines in L2 until evicted, so a line written in parts by different
+// instructions leaves as one write: the flat kernel's lines at row starts.
+// kStorePlain: lane-strided patterns, where non-temporal stores measured 3x
+// slower.
+enum StorePolicy : int { kStorePlain = 0, kStoreNt = 1, kStoreSys = 2 };
+constexpr int kTilesStore = FN_NT_STORE;
+
+// Stores NE output values as 16-, 8- or 4-byte vectors; 16-byte vectors
+// with the cache policy kPolicy.
+template <typename OutT, int NE, int kPolicy = kStorePlain>
 __device__ __forceinline__ void store_group(OutT* __restrict__ dst, const float (&v)[NE]) {
   constexpr int kBytes = NE * (int)sizeof(OutT);
   constexpr int kWords = kBytes / 4;
@@ -252,9 +260,9 @@ __device__ __forceinline__ void store_group(OutT* __restrict__ dst, const float 
     for (int s = 0; s < kWords / 4; ++s) {
       const u32x4 q = {u[4 * s], u[4 * s + 1], u[4 * s + 2], u[4 * s + 3]};
       u32x4* p = reinterpret_cast<u32x4*>(dst) + s;
-      if constexpr (kStream && FN_NT_STORE == 1) {
+      if constexpr (kPolicy == kStoreNt) {
         __builtin_nontemporal_store(q, p);
-      } else if constexpr (kStream && FN_NT_STORE == 2) {
+      } else if constexpr (kPolicy == kStoreSys) {
         stream_store16(p, q);
       } else {
         *p = q;
@@ -750,7 +758,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
             for (int32_t r = slot_row; r < T.rows; r += rpi) {
               float v[E];
               cs.template values<kSrc>(s_lds, row_lds(r), P, T.h0 + r, v);
-              store_group<OutT, E, true>(out + (int64_t)r * row_out + cs.x0, v);
+              store_group<OutT, E, kTilesStore>(out + (int64_t)r * row_out + cs.x0, v);
             }
           } else {
             // compact rows: LDS start and output advance by fixed steps
@@ -759,7 +767,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
             for (int32_t r = slot_row; r < T.rows; r += rpi) {
               float v[E];
               cs.template values<kSrc>(s_lds, lds, P, T.h0 + r, v);
-              store_group<OutT, E, true>(dst, v);
+              store_group<OutT, E, kTilesStore>(dst, v);
               lds += rpi * row;
               dst += (int64_t)rpi * row_out;
             }
@@ -783,7 +791,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
           const SampleParams P = s_params[slot];
           float v[E];
           cs.values(s_lds, row_lds(r), P, h, v);
-          store_group<OutT, E, true>(out + (int64_t)r * row_out + cs.x0, v);
+          store_group<OutT, E, kTilesStore>(out + (int64_t)r * row_out + cs.x0, v);
         }
       }
     }
@@ -806,7 +814,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
         for (int32_t r = 0; r < T.rows; ++r) {
           float v[E];
           cs.template values<kSrc>(s_lds, row_lds(r), P, T.h0 + r, v);
-          store_group<OutT, E, true>(out + (int64_t)r * row_out + cs.x0, v);
+          store_group<OutT, E, kTilesStore>(out + (int64_t)r * row_out + cs.x0, v);
         }
       }
     };
@@ -832,7 +840,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       const Setup cq(a, x0);
       float v[E];
       cq.values(s_lds, row_lds((int32_t)r), P, h, v);
-      store_group<OutT, E, true>(out + off, v);
+      store_group<OutT, E, kTilesStore>(out + off, v);
     }
   }
 }
@@ -900,7 +908,9 @@ __device__ __forceinline__ void flat_elements(const FusedArgs& a, const Tile& T,
 // of its own, so that the few of them neither hold up whole wavefronts of the
 // first pass nor leave a few lanes working alone.  Only the tile's own
 // elements are stored: the tile next to it stores the rest of a vector they
-// share, so no byte is written twice.
+// share, so no byte is written twice.  All stores are non-temporal
+// (kStoreNt): the lines that the two passes (or two tiles) write in parts
+// then merge in L2 instead of reaching memory as partial writes.
 template <int C, typename OutT, bool kPad4, bool kComp>
 __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(FusedArgs a) {
   constexpr int kThreads = tiles_threads<OutT>();
@@ -935,11 +945,12 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
     if (all_elements) {
       flat_elements<C, OC, E, kComp>(a, T, s_lds, s_params, head, l0, count, v);
       if (l0 >= 0 && l0 + E <= count) {
-        store_group<OutT, E, true>(out + e0, v);
+        store_group<OutT, E, kStoreNt>(out + e0, v);
       } else {
 #pragma unroll
         for (int k = 0; k < E; ++k)
-          if (l0 + k >= 0 && l0 + k < count) out[e0 + k] = to_out<OutT>(v[k]);
+          if (l0 + k >= 0 && l0 + k < count)
+            __builtin_nontemporal_store(to_out<OutT>(v[k]), out + e0 + k);
       }
       continue;
     }
@@ -959,7 +970,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
       cs.template values<kSrcFlip>(s_lds, staged_row(a, T, head, row, r), P, h, v);
     else
       cs.template values<kSrcBytes>(s_lds, staged_row(a, T, head, row, r), P, h, v);
-    store_group<OutT, E, true>(out + e0, v);
+    store_group<OutT, E, kStoreNt>(out + e0, v);
   }
   if (all_elements) return;
 
@@ -981,7 +992,8 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
     const int64_t e0 = kv * E - mu;
     const int32_t l = (int32_t)(e0 - f0) + k;
     if (l < 0 || l >= count) continue;
-    out[e0 + k] = to_out<OutT>(flat_element<C, OC, kComp>(a, T, s_lds, s_params, head, l));
+    __builtin_nontemporal_store(
+        to_out<OutT>(flat_element<C, OC, kComp>(a, T, s_lds, s_params, head, l)), out + e0 + k);
   }
 }
 
