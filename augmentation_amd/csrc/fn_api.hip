@@ -252,7 +252,7 @@ void launch_grouped_px(const fn::FusedArgs& a, int C, int out_dtype, unsigned gr
 }
 
 template <int C, bool kComp>
-void launch_tiles_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t lds,
+void launch_tiles_c(const fn::FusedArgs& a, int out_dtype, bool nt, unsigned grid, size_t lds,
                     hipStream_t st) {
   if (out_dtype == FN_OUT_FP32)
     fn::fused_tiles_kernel<C, float, false, kComp>
@@ -260,28 +260,32 @@ void launch_tiles_c(const fn::FusedArgs& a, int out_dtype, unsigned grid, size_t
   else if (out_dtype == FN_OUT_FP16_PAD4)
     fn::fused_tiles_kernel<C, _Float16, true, kComp>
         <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
+  else if (nt)
+    fn::fused_tiles_kernel<C, _Float16, false, kComp, fn::kStoreNt>
+        <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
   else
     fn::fused_tiles_kernel<C, _Float16, false, kComp>
         <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
 }
 
 template <bool kComp>
-void launch_tiles_k(const fn::FusedArgs& a, int C, int out_dtype, unsigned grid, size_t lds,
-                    hipStream_t st) {
+void launch_tiles_k(const fn::FusedArgs& a, int C, int out_dtype, bool nt, unsigned grid,
+                    size_t lds, hipStream_t st) {
   switch (C) {
-    case 1: launch_tiles_c<1, kComp>(a, out_dtype, grid, lds, st); break;
-    case 2: launch_tiles_c<2, kComp>(a, out_dtype, grid, lds, st); break;
-    case 3: launch_tiles_c<3, kComp>(a, out_dtype, grid, lds, st); break;
-    default: launch_tiles_c<4, kComp>(a, out_dtype, grid, lds, st); break;
+    case 1: launch_tiles_c<1, kComp>(a, out_dtype, nt, grid, lds, st); break;
+    case 2: launch_tiles_c<2, kComp>(a, out_dtype, nt, grid, lds, st); break;
+    case 3: launch_tiles_c<3, kComp>(a, out_dtype, nt, grid, lds, st); break;
+    default: launch_tiles_c<4, kComp>(a, out_dtype, nt, grid, lds, st); break;
   }
 }
 
-void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, bool comp, unsigned grid,
+// nt: the non-temporal-store instance for long packed fp16 launches
+void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, bool comp, bool nt, unsigned grid,
                   size_t lds, hipStream_t st) {
   if (comp)
-    launch_tiles_k<true>(a, C, out_dtype, grid, lds, st);
+    launch_tiles_k<true>(a, C, out_dtype, nt, grid, lds, st);
   else
-    launch_tiles_k<false>(a, C, out_dtype, grid, lds, st);
+    launch_tiles_k<false>(a, C, out_dtype, nt, grid, lds, st);
 }
 
 template <int C, bool kComp>
@@ -607,7 +611,11 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
     // 16-byte aligned output; any other element-aligned output takes the
     // flat layout
     if ((uintptr_t)out_dev % 16 == 0 && row_out % (16 / out_bytes) == 0) {
-      launch_tiles(a, C, out_dtype, comp, (unsigned)a.total_tiles, lds, st);
+      // algorithmic bytes of the launch: input read once, output written once
+      const int64_t moved = elems + out_elems * out_bytes;
+      const bool nt = out_dtype == FN_OUT_FP16 && fn::kTilesNtMinBytes > 0 &&
+                      moved >= fn::kTilesNtMinBytes;
+      launch_tiles(a, C, out_dtype, comp, nt, (unsigned)a.total_tiles, lds, st);
       return launch_status("fused_tiles_kernel launch");
     }
     launch_flat(a, C, out_dtype, comp, (unsigned)a.total_tiles, lds, st);

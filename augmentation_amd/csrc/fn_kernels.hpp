@@ -48,6 +48,8 @@ namespace fn {
 // and of the tiles kernel's lane-contiguous stores:
 //   FN_NT_STORE      policy of its 16-byte stores: 0 default, 1
 //                    non-temporal, 2 streaming system-scope (sc0 sc1 nt)
+//   FN_NT_MIN_BYTES  packed fp16 launches moving at least this many bytes
+//                    store non-temporal instead (0: never)
 #ifndef FN_GROUP_PX_MAX
 #define FN_GROUP_PX_MAX 16
 #endif
@@ -56,6 +58,9 @@ namespace fn {
 #endif
 #ifndef FN_NT_STORE
 #define FN_NT_STORE 2
+#endif
+#ifndef FN_NT_MIN_BYTES
+#define FN_NT_MIN_BYTES 335544320
 #endif
 
 // Tiles kernel (defaults chosen by measurement):
@@ -229,13 +234,18 @@ __device__ __forceinline__ void stream_store16(u32x4* p, u32x4 q) {
 
 // Cache policy of a 16-byte output store.  kStoreSys (sc0 sc1 nt) writes
 // through to memory at system scope: fastest where every 128-byte line is
-// written whole by one store instruction (the tiles kernel).  kStoreNt
-// leaves lines in L2 until evicted, so a line written in parts by different
-// instructions leaves as one write: the flat kernel's lines at row starts.
-// kStorePlain: lane-strided patterns, where non-temporal stores measured 3x
-// slower.
+// written whole by one store instruction (the tiles kernel) and the launch
+// is short.  kStoreNt leaves lines in L2 until evicted: a line written in
+// parts by different instructions leaves as one write (the flat kernel's
+// lines at row starts), and long packed-fp16 launches stream faster
+// (kTilesNtMinBytes).  kStorePlain: lane-strided patterns, where
+// non-temporal stores measured 3x slower.
 enum StorePolicy : int { kStorePlain = 0, kStoreNt = 1, kStoreSys = 2 };
 constexpr int kTilesStore = FN_NT_STORE;
+// Packed fp16 launches of at least this many algorithmic bytes store with
+// kStoreNt (measured on 224x224x3 batches: 2.5% faster at 2,048 images,
+// 1-1.7% at 1,024, 1% slower at 512 and 256); 0: never.
+constexpr int64_t kTilesNtMinBytes = FN_NT_MIN_BYTES;
 
 // Stores NE output values as 16-, 8- or 4-byte vectors; 16-byte vectors
 // with the cache policy kPolicy.
@@ -710,8 +720,9 @@ __device__ __forceinline__ int32_t staged_row(const FusedArgs& a, const Tile& T,
 // bytes) once.  Many small independent work-groups per compute unit hide the
 // memory latency.
 // Requires W*OC a multiple of E (OC = 4 when kPad4, else C) and a 16-byte
-// aligned output; the input may be compact or strided (a.strided).
-template <int C, typename OutT, bool kPad4, bool kComp>
+// aligned output; the input may be compact or strided (a.strided).  kStore:
+// the cache policy of the stores.
+template <int C, typename OutT, bool kPad4, bool kComp, int kStore = kTilesStore>
 __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(FusedArgs a) {
   constexpr int kThreads = tiles_threads<OutT>();
   constexpr int kWaves = kThreads / 64;
@@ -758,7 +769,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
             for (int32_t r = slot_row; r < T.rows; r += rpi) {
               float v[E];
               cs.template values<kSrc>(s_lds, row_lds(r), P, T.h0 + r, v);
-              store_group<OutT, E, kTilesStore>(out + (int64_t)r * row_out + cs.x0, v);
+              store_group<OutT, E, kStore>(out + (int64_t)r * row_out + cs.x0, v);
             }
           } else {
             // compact rows: LDS start and output advance by fixed steps
@@ -767,7 +778,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
             for (int32_t r = slot_row; r < T.rows; r += rpi) {
               float v[E];
               cs.template values<kSrc>(s_lds, lds, P, T.h0 + r, v);
-              store_group<OutT, E, kTilesStore>(dst, v);
+              store_group<OutT, E, kStore>(dst, v);
               lds += rpi * row;
               dst += (int64_t)rpi * row_out;
             }
@@ -791,7 +802,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
           const SampleParams P = s_params[slot];
           float v[E];
           cs.values(s_lds, row_lds(r), P, h, v);
-          store_group<OutT, E, kTilesStore>(out + (int64_t)r * row_out + cs.x0, v);
+          store_group<OutT, E, kStore>(out + (int64_t)r * row_out + cs.x0, v);
         }
       }
     }
@@ -814,7 +825,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
         for (int32_t r = 0; r < T.rows; ++r) {
           float v[E];
           cs.template values<kSrc>(s_lds, row_lds(r), P, T.h0 + r, v);
-          store_group<OutT, E, kTilesStore>(out + (int64_t)r * row_out + cs.x0, v);
+          store_group<OutT, E, kStore>(out + (int64_t)r * row_out + cs.x0, v);
         }
       }
     };
@@ -840,7 +851,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       const Setup cq(a, x0);
       float v[E];
       cq.values(s_lds, row_lds((int32_t)r), P, h, v);
-      store_group<OutT, E, kTilesStore>(out + off, v);
+      store_group<OutT, E, kStore>(out + off, v);
     }
   }
 }
