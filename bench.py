@@ -408,6 +408,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming reference")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the two-stream pipeline (whose overlapping launches would "
+                         "otherwise share a kernel trace with the one-stream ones)")
     ap.add_argument("--sweep", default=None, metavar="N,N,...",
                     help="time the headline shape at these batch sizes (and the streaming "
                          "reference and a minimal launch) instead of the JSON line")
@@ -509,7 +512,7 @@ def main() -> int:
         line["stream_ceiling"] = {"gbs": round(c["gbs"], 1), "bytes_per_launch": c["bytes"],
                                   "ms": round(c["ms"], 5),
                                   "fused_vs_stream": round(achieved / c["gbs"], 4)}
-    if not args.no_stream and w.launches == 1:
+    if not args.no_stream and not args.no_pipeline and w.launches == 1:
         line["two_stream_pipeline"] = bench_two_streams(b, w, args.steps, args.warmup, sets,
                                                         args.prewarm_seconds)
     if args.all:
