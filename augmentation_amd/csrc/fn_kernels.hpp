@@ -68,6 +68,8 @@ namespace fn {
 //   FN_MIN_TILE_BYTES  smallest tile the plan shrinks to for small batches
 //   FN_WGS_PER_CU      most work-groups resident on a compute unit (0: no
 //                      cap); enforced through the LDS size each requests
+//   FN_XCD_RUN         consecutive tiles one XCD takes in turn (1: tile =
+//                      work-group index)
 #ifndef FN_TILE_BYTES
 #define FN_TILE_BYTES 8192
 #endif
@@ -77,12 +79,16 @@ namespace fn {
 #ifndef FN_WGS_PER_CU
 #define FN_WGS_PER_CU 6
 #endif
+#ifndef FN_XCD_RUN
+#define FN_XCD_RUN 16
+#endif
 
 
 constexpr int kBlock = 256;             // four wave64 wavefronts
 constexpr int kTileBytesTarget = FN_TILE_BYTES;
 constexpr int kMinTileBytes = FN_MIN_TILE_BYTES;
 constexpr int kWgsPerCu = FN_WGS_PER_CU;
+constexpr uint32_t kXcdRun = FN_XCD_RUN;
 constexpr int kMaxImagesPerBlock = 16;  // images whose decisions one work-group draws
 constexpr int kMaxIter = FN_GROUP_ITER;  // pixel groups per lane in the grouped kernel
 constexpr int kGroupPxMax = FN_GROUP_PX_MAX;
@@ -394,6 +400,23 @@ struct Tile {
   int64_t start;    // offset of the tile's first byte in the compact layout
   int32_t len;      // bytes of the tile in the compact layout (rows * W * C)
 };
+
+// The tile work-group b takes.  The dispatcher deals work-groups round-robin
+// over the chip's 8 XCDs (b to XCD b mod 8), each with its own L2; with
+// tile = b, neighbouring tiles, which share the 128-byte lines at their
+// common edge, would always run on different XCDs.  Within each block of
+// 8 * kXcdRun work-groups, work-group o takes tile (o mod 8) * kXcdRun +
+// o / 8: every XCD works through runs of kXcdRun consecutive tiles, and the
+// tiles in flight stay one contiguous front of the batch.  The grid's last
+// partial block keeps tile = b.  Measured (runs of 16 against 1): 0.2-1.2%
+// faster; runs of 32-128 are slower, and eighths of the batch per XCD 6-12%
+// slower.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t grid) {
+  constexpr uint32_t kBlockTiles = 8u * kXcdRun;
+  if (kXcdRun <= 1u || b >= grid / kBlockTiles * kBlockTiles) return b;
+  const uint32_t base = b / kBlockTiles * kBlockTiles, o = b - base;
+  return base + (o % 8u) * kXcdRun + o / 8u;
+}
 
 __device__ __forceinline__ Tile tile_at(const FusedArgs& a, uint32_t t) {
   Tile T;
@@ -733,7 +756,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   extern __shared__ __align__(16) uint8_t s_lds[];
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
-  const Tile T = tile_at(a, blockIdx.x);
+  const Tile T = tile_at(a, xcd_tile(blockIdx.x, gridDim.x));
   stage_tile<kWaves>(a, T, s_lds, s_params);
 
   const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
@@ -932,7 +955,7 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
   extern __shared__ __align__(16) uint8_t s_lds[];
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
-  const Tile T = tile_at(a, blockIdx.x);
+  const Tile T = tile_at(a, xcd_tile(blockIdx.x, gridDim.x));
   stage_tile<kWaves>(a, T, s_lds, s_params);
 
   const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
