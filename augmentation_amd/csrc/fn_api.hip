@@ -257,6 +257,9 @@ void launch_tiles_c(const fn::FusedArgs& a, int out_dtype, bool nt, unsigned gri
   if (out_dtype == FN_OUT_FP32)
     fn::fused_tiles_kernel<C, float, false, kComp>
         <<<grid, fn::tiles_threads<float>(), lds, st>>>(a);
+  else if (out_dtype == FN_OUT_FP16_PAD4 && nt)
+    fn::fused_tiles_kernel<C, _Float16, true, kComp, fn::kStoreNt>
+        <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
   else if (out_dtype == FN_OUT_FP16_PAD4)
     fn::fused_tiles_kernel<C, _Float16, true, kComp>
         <<<grid, fn::tiles_threads<_Float16>(), lds, st>>>(a);
@@ -279,7 +282,7 @@ void launch_tiles_k(const fn::FusedArgs& a, int C, int out_dtype, bool nt, unsig
   }
 }
 
-// nt: the non-temporal-store instance for long packed fp16 launches
+// nt: the non-temporal-store instance for long fp16 launches (packed or padded)
 void launch_tiles(const fn::FusedArgs& a, int C, int out_dtype, bool comp, bool nt, unsigned grid,
                   size_t lds, hipStream_t st) {
   if (comp)
@@ -613,7 +616,7 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
     if ((uintptr_t)out_dev % 16 == 0 && row_out % (16 / out_bytes) == 0) {
       // algorithmic bytes of the launch: input read once, output written once
       const int64_t moved = elems + out_elems * out_bytes;
-      const bool nt = out_dtype == FN_OUT_FP16 && fn::kTilesNtMinBytes > 0 &&
+      const bool nt = out_dtype != FN_OUT_FP32 && fn::kTilesNtMinBytes > 0 &&
                       moved >= fn::kTilesNtMinBytes;
       launch_tiles(a, C, out_dtype, comp, nt, (unsigned)a.total_tiles, lds, st);
       return launch_status("fused_tiles_kernel launch");

@@ -48,8 +48,8 @@ namespace fn {
 // and of the tiles kernel's lane-contiguous stores:
 //   FN_NT_STORE      policy of its 16-byte stores: 0 default, 1
 //                    non-temporal, 2 streaming system-scope (sc0 sc1 nt)
-//   FN_NT_MIN_BYTES  packed fp16 launches moving at least this many bytes
-//                    store non-temporal instead (0: never)
+//   FN_NT_MIN_BYTES  fp16 launches moving at least this many bytes store
+//                    non-temporal instead (0: never)
 #ifndef FN_GROUP_PX_MAX
 #define FN_GROUP_PX_MAX 16
 #endif
@@ -243,14 +243,16 @@ __device__ __forceinline__ void stream_store16(u32x4* p, u32x4 q) {
 // written whole by one store instruction (the tiles kernel) and the launch
 // is short.  kStoreNt leaves lines in L2 until evicted: a line written in
 // parts by different instructions leaves as one write (the flat kernel's
-// lines at row starts), and long packed-fp16 launches stream faster
+// lines at row starts), and long fp16 launches stream faster
 // (kTilesNtMinBytes).  kStorePlain: lane-strided patterns, where
 // non-temporal stores measured 3x slower.
 enum StorePolicy : int { kStorePlain = 0, kStoreNt = 1, kStoreSys = 2 };
 constexpr int kTilesStore = FN_NT_STORE;
-// Packed fp16 launches of at least this many algorithmic bytes store with
-// kStoreNt (measured on 224x224x3 batches: 2.5% faster at 2,048 images,
-// 1-1.7% at 1,024, 1% slower at 512 and 256); 0: never.
+// fp16 launches (packed or 4-channel) of at least this many algorithmic
+// bytes store with kStoreNt; 0: never.  Measured on 224x224x3 batches:
+// packed 2.5% faster at 2,048 images, 1-1.7% at 1,024, 1% slower at 512 and
+// 256; 4-channel 2% faster at 2,048 and 0.6-1.7% at 1,024; fp32 output 1-2%
+// slower at every size, so it keeps kTilesStore.
 constexpr int64_t kTilesNtMinBytes = FN_NT_MIN_BYTES;
 
 // Stores NE output values as 16-, 8- or 4-byte vectors; 16-byte vectors

@@ -150,26 +150,28 @@ def test_slices_reproduce_the_whole_batch(b, out_dtype):
                        plain.view(torch.int16 if out_dtype else torch.int32))
 
 
-@pytest.mark.parametrize("C", [1, 2, 3, 4])
-def test_long_launch_equals_its_short_slices(b, C):
-    """A packed fp16 launch long enough for the non-temporal-store instance
-    of the tiles kernel (at least 320 MiB moved) equals the same batch done
-    as slices of at most 256 images (the system-scope-store instance), bit
-    for bit."""
+@pytest.mark.parametrize("C,out_dtype", [(1, 1), (2, 1), (3, 1), (4, 1), (1, 2), (3, 2)])
+def test_long_launch_equals_its_short_slices(b, C, out_dtype):
+    """An fp16 launch (packed or 4-channel) long enough for the
+    non-temporal-store instance of the tiles kernel (at least 320 MiB moved)
+    equals the same batch done as slices of at most 128 images (the
+    system-scope-store instance), bit for bit."""
     H = W = 224
-    N = -(-(320 << 20) // (H * W * C * 3)) + 3
-    say(f"long launch: N={N} C={C}")
+    oc = 4 if out_dtype == 2 else C
+    N = -(-(320 << 20) // (H * W * (C + 2 * oc))) + 3
+    say(f"long launch: N={N} C={C} out_dtype={out_dtype}")
     g = torch.Generator(device="cuda").manual_seed(C)
     xt = torch.randint(0, 256, (N, H, W, C), dtype=torch.uint8, device="cuda", generator=g)
     mean, std = (0.485, 0.456, 0.406, 0.5)[:C], (0.229, 0.224, 0.225, 0.25)[:C]
     args = (mean, std, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, 99)
-    whole = torch.empty((N, H, W, C), dtype=torch.float16, device="cuda")
+    whole = torch.empty((N, H, W, oc), dtype=torch.float16, device="cuda")
     parts = torch.empty_like(whole)
     row, img = W * C, H * W * C
-    b.fn_fused_normalize_ex(xt, row, img, N, H, W, C, *args, 0, 1, whole)
-    for a_ in range(0, N, 256):
-        b_ = min(N, a_ + 256)
-        b.fn_fused_normalize_ex(xt[a_:b_], row, img, b_ - a_, H, W, C, *args, a_, 1, parts[a_:b_])
+    b.fn_fused_normalize_ex(xt, row, img, N, H, W, C, *args, 0, out_dtype, whole)
+    for a_ in range(0, N, 128):
+        b_ = min(N, a_ + 128)
+        b.fn_fused_normalize_ex(xt[a_:b_], row, img, b_ - a_, H, W, C, *args, a_, out_dtype,
+                                parts[a_:b_])
     torch.cuda.synchronize()
     assert torch.equal(whole.view(torch.int16), parts.view(torch.int16))
 
