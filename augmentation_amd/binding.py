@@ -45,15 +45,36 @@ _SIGS = {
     "fn_test_erase_dims": [_P, _P, _i64, _i32, _i32, _f32, _f32, _f32, _f32, _P, _P, _P, _P],
     "fn_test_cr_ops": [_i32, _P, _P, _i64, _P, _P],
     "fn_test_stream": [_P, _P, _i64, _i32, _P],
+    "fn_test_timeline": [_P, _i64],
 }
-for _name, _args in _SIGS.items():
-    getattr(_lib, _name).argtypes = _args
-    getattr(_lib, _name).restype = ctypes.c_int
-_lib.fn_last_error.argtypes = []
-_lib.fn_last_error.restype = ctypes.c_char_p
+
+
+def _declare(lib) -> None:
+    for name, args in _SIGS.items():
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fn_last_error.argtypes = []
+    lib.fn_last_error.restype = ctypes.c_char_p
+
+
+_declare(_lib)
 
 EXPORTED = ("fn_fused_normalize", "fn_fused_normalize_ex", "fn_params", "fn_params_ex",
-            "fn_last_error", "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_stream")
+            "fn_last_error", "fn_test_erase_dims", "fn_test_cr_ops", "fn_test_stream",
+            "fn_test_timeline")
+
+TIMELINE_LIB_PATH = os.path.join(_HERE, "libfn_timeline.so")
+
+
+def timeline_library():
+    """The instrumented build libfn_timeline.so (same entry points; its
+    tiles kernel records per-tile clock stamps, see fn_test_timeline), as a
+    ctypes handle.  A measurement tool: the product path is libfn.so."""
+    if not os.path.exists(TIMELINE_LIB_PATH):
+        raise ImportError(f"{TIMELINE_LIB_PATH} is not built")
+    lib = ctypes.CDLL(TIMELINE_LIB_PATH)
+    _declare(lib)
+    return lib
 
 
 class FnError(RuntimeError):
@@ -143,6 +164,11 @@ def fn_test_cr_ops(op, a, b, count, out, stream=None) -> int:
 
 def fn_test_stream(src, dst, in_bytes, widen, stream=None) -> int:
     return _check(_lib.fn_test_stream(_addr(src), _addr(dst), in_bytes, widen, _stream(stream)))
+
+
+def fn_test_timeline(stamps, tiles) -> int:
+    """libfn.so records no timeline: this raises FnError (FN_EINVAL)."""
+    return _check(_lib.fn_test_timeline(_addr(stamps), tiles))
 
 
 # ------------------------------------------------------------ tensor helpers

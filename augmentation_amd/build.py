@@ -24,6 +24,9 @@ HEADERS = [os.path.join(HERE, "csrc", h) for h in ("fn_device.hpp", "fn_kernels.
                                                    "exp2_table.inc")] + [
     os.path.join(ROOT, "include", "fn.h")]
 LIB_PATH = os.path.join(HERE, "libfn.so")
+# the instrumented build: the tiles kernel records per-tile clock stamps
+# (fn_test_timeline); a measurement tool, never the product library
+TIMELINE_LIB_PATH = os.path.join(HERE, "libfn_timeline.so")
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
@@ -53,10 +56,12 @@ def build_cpu(verbose: bool = False) -> str:
     return CPU_LIB_PATH
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Compile the library (always recompiles) and return its path;
+    timeline: the instrumented build libfn_timeline.so instead."""
+    path = TIMELINE_LIB_PATH if timeline else LIB_PATH
+    tmp = path + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(["-DFN_TIMELINE=1"] if timeline else []), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,10 +71,11 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, path)
+    return path
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, timeline=True))
     print(build_cpu(verbose=True))

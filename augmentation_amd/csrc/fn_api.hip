@@ -484,6 +484,13 @@ FN_EXPORT int fn_params(uint64_t seed, int64_t N, int32_t H, int32_t W, float fl
 
 namespace {
 
+#if FN_TIMELINE
+// where the tiles kernel of later launches records its stamps (instrumented
+// builds only; set by fn_test_timeline)
+uint64_t* g_timeline = nullptr;
+int64_t g_timeline_tiles = 0;
+#endif
+
 // Both fused entry points.  strides == nullptr: the compact layout; else
 // {row stride, image stride} of the source in bytes.
 int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64_t N, int32_t H,
@@ -495,6 +502,10 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
   int rc = make_draw_args(seed, H, W, flip_p, erase_p, scale_min, scale_max, ratio_min, ratio_max,
                           &a.draw);
   if (rc) return rc;
+#if FN_TIMELINE
+  a.timeline = g_timeline;
+  a.timeline_tiles = g_timeline_tiles;
+#endif
   if (C < 1 || C > 4) return fail(FN_EINVAL, "C must be in 1..4 (got %d)", C);
   if (N < 0) return fail(FN_EINVAL, "N must be >= 0");
   if (first_sample_id < 0) return fail(FN_EINVAL, "first_sample_id must be >= 0");
@@ -716,6 +727,27 @@ FN_EXPORT int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev,
   fn::cr_ops_kernel<<<blocks_for(count, fn::kBlock), fn::kBlock, 0, (hipStream_t)stream>>>(
       op, a_dev, op == 2 ? b_dev : a_dev, count, out_dev);
   return launch_status("cr_ops_kernel launch");
+}
+
+FN_EXPORT int fn_test_timeline(void* stamps_dev, int64_t tiles) {
+#if FN_TIMELINE
+  if (tiles < 0) return fail(FN_EINVAL, "tiles must be >= 0");
+  if (tiles > ((int64_t)1 << 31)) return fail(FN_EOVERFLOW, "tiles too large");
+  if (tiles > 0) {
+    if (stamps_dev == nullptr) return fail(FN_EINVAL, "stamps_dev must not be NULL");
+    int dev = -1;
+    const int rc = check_device_range(stamps_dev, (size_t)tiles * 4 * sizeof(uint64_t),
+                                      "stamps_dev", &dev);
+    if (rc) return rc;
+  }
+  g_timeline = tiles > 0 ? reinterpret_cast<uint64_t*>(stamps_dev) : nullptr;
+  g_timeline_tiles = tiles;
+  return ok();
+#else
+  (void)stamps_dev;
+  (void)tiles;
+  return fail(FN_EINVAL, "this library records no timeline (libfn_timeline.so does)");
+#endif
 }
 
 FN_EXPORT int fn_test_stream(const void* src_dev, void* dst_dev, int64_t in_bytes, int32_t widen,

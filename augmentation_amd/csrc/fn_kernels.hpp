@@ -82,6 +82,12 @@ namespace fn {
 #ifndef FN_XCD_RUN
 #define FN_XCD_RUN 16
 #endif
+// FN_TIMELINE 1: the instrumented build (libfn_timeline.so), whose tiles
+// kernel records four real-time-clock stamps per tile (fn_test_timeline);
+// the product library is built with 0.
+#ifndef FN_TIMELINE
+#define FN_TIMELINE 0
+#endif
 
 
 constexpr int kBlock = 256;             // four wave64 wavefronts
@@ -146,6 +152,10 @@ struct FusedArgs {
   float mul[4], mul_lo[4];
   float nsub[4], nsub_lo[4];
   DrawArgs draw;
+#if FN_TIMELINE
+  uint64_t* timeline;      // 4 stamps per tile, tiles < timeline_tiles
+  int64_t timeline_tiles;  // 0: no recording
+#endif
 };
 
 // (x/255 - mean)/std of one byte x from the constant pairs m = mh + ml
@@ -736,6 +746,28 @@ __device__ __forceinline__ int32_t staged_row(const FusedArgs& a, const Tile& T,
   return head + r * row;
 }
 
+#if FN_TIMELINE
+// Instrumented builds: the stamps of tile t, from the 100 MHz real-time
+// clock: work-group start, staged (after the staging barrier), stores
+// issued (wavefront 0) and stores acknowledged (every wavefront, after
+// waiting for its stores).  The wait and barrier at the end are the only
+// work the instrumentation adds.
+__device__ __forceinline__ void timeline_record(const FusedArgs& a, uint32_t t, uint64_t start,
+                                                uint64_t staged) {
+  const uint64_t issued = __builtin_amdgcn_s_memrealtime();
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const uint64_t acked = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0 && a.timeline != nullptr && (int64_t)t < a.timeline_tiles) {
+    uint64_t* d = a.timeline + 4 * (size_t)t;
+    d[0] = start;
+    d[1] = staged;
+    d[2] = issued;
+    d[3] = acked;
+  }
+}
+#endif
+
 // The fused pass, one tile per work-group (grid = total_tiles): the tile is
 // staged (stage_tile), then every lane makes E = 16/sizeof(OutT) consecutive
 // output elements of a row at a time (two whole 4-channel pixels when kPad4)
@@ -758,8 +790,15 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
   extern __shared__ __align__(16) uint8_t s_lds[];
   __shared__ SampleParams s_params[kMaxImagesPerBlock];
 
-  const Tile T = tile_at(a, xcd_tile(blockIdx.x, gridDim.x));
+#if FN_TIMELINE
+  const uint64_t tl_start = __builtin_amdgcn_s_memrealtime();
+#endif
+  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const Tile T = tile_at(a, tile);
   stage_tile<kWaves>(a, T, s_lds, s_params);
+#if FN_TIMELINE
+  const uint64_t tl_staged = __builtin_amdgcn_s_memrealtime();
+#endif
 
   const int32_t head = (int32_t)(((uintptr_t)a.in + (uintptr_t)T.start) & 15u);
   const int32_t row = a.W * C;        // input bytes of a row
@@ -879,6 +918,9 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_tiles_kernel(Fuse
       store_group<OutT, E, kStore>(out + off, v);
     }
   }
+#if FN_TIMELINE
+  timeline_record(a, tile, tl_start, tl_staged);
+#endif
 }
 
 // Normalized value of input byte x in channel c (a lane-varying c < C).

@@ -331,6 +331,112 @@ def sweep(b, steps: int, warmup: int, prewarm_s: float, sizes) -> None:
                           "streaming_tbs": round(3 * img / (per * 1e-6) / 1e12, 3)}), flush=True)
 
 
+def timeline(b, steps: int, warmup: int, prewarm_s: float, launches: int = 20) -> None:
+    """Where the headline launch's microseconds go, from the instrumented
+    build libfn_timeline.so: every tile's work-group records the 100 MHz
+    real-time clock at its start, after staging (tile loaded, decisions
+    drawn), when its stores are issued and when they are acknowledged
+    (fn_test_timeline).  Each recorded launch is the last of 10 back-to-back
+    ones over the rotating buffer sets.  Prints a text summary."""
+    import numpy as np
+    import torch
+    from augmentation_amd import synth
+    lib = b.timeline_library()
+    st = torch.cuda.current_stream()
+    w = synth.WORKLOADS[synth.HEADLINE]
+    sets = 10
+    x = torch.from_numpy(w.make_input()).cuda()
+    ins = [x] + [x.clone() for _ in range(sets - 1)]
+    outs = [torch.empty(w.out_shape, dtype=torch.float16, device="cuda") for _ in range(sets)]
+    max_tiles = w.N * w.H  # a tile holds whole rows
+    stamps = torch.zeros(max_tiles * 4, dtype=torch.int64, device="cuda")
+    mean, std = b._host_floats(w.mean, w.C), b._host_floats(w.std, w.C)
+
+    def launch(L, k):
+        rc = L.fn_fused_normalize(ins[k].data_ptr(), w.N, w.H, w.W, w.C, mean, std, w.flip_p,
+                                  w.erase_p, w.scale[0], w.scale[1], w.ratio[0], w.ratio[1],
+                                  w.seeds[0], w.out_dtype, outs[k].data_ptr(), st.cuda_stream)
+        if rc:
+            raise b.FnError(rc, L.fn_last_error().decode())
+
+    ms_prod = time_launches(lambda k: launch(b._lib, k), steps, warmup, sets, st, prewarm_s)
+    if lib.fn_test_timeline(stamps.data_ptr(), max_tiles):
+        raise b.FnError(-1, lib.fn_last_error().decode())
+    ms_inst = time_launches(lambda k: launch(lib, k), steps, warmup, sets, st, prewarm_s)
+    runs = []
+    for _ in range(launches):
+        stamps.zero_()
+        for k in range(10):
+            launch(lib, k % sets)
+        torch.cuda.synchronize()
+        d = stamps.view(-1, 4).cpu().numpy()
+        runs.append(d[d[:, 0] != 0].astype(np.float64))
+    lib.fn_test_timeline(None, 0)
+    tiles = len(runs[0])
+    in_tile = w.N * w.H * w.W * w.C / tiles  # bytes per tile, on average
+    out_tile = in_tile * 2
+    tick = 0.01  # microseconds per tick of the 100 MHz clock
+
+    spans, phase, occ_rows, first_gen, last_start, tail_half, rate_all, rate_mid = \
+        [], {"stage": [], "compute": [], "drain": [], "life": []}, [], [], [], [], [], []
+    for d in runs:
+        t0 = d[:, 0].min()
+        S, G, I, A = [(d[:, k] - t0) * tick for k in range(4)]
+        span = A.max()
+        spans.append(span)
+        for name, v in (("stage", G - S), ("compute", I - G), ("drain", A - I), ("life", A - S)):
+            phase[name].append(v)
+        grid = np.arange(0.0, span + 0.5, 0.5)
+        active = np.array([np.sum((S <= t) & (A > t)) for t in grid])
+        occ_rows.append(active)
+        peak = active.max()
+        gen = S <= 0.3
+        first_gen.append((int(gen.sum()), np.percentile(A[gen], [10, 50, 90])))
+        last_start.append(S.max())
+        tail_half.append(span - grid[np.nonzero(active >= peak / 2)[0].max()])
+        # modelled traffic: each tile's reads spread evenly over its staging,
+        # its writes over the rest of its life
+        fine = np.arange(0.0, span, 0.05)
+        rd = np.zeros_like(fine)
+        wr = np.zeros_like(fine)
+        for s_, g_, a_ in zip(S, G, A):
+            i0, i1, i2 = (int(v / 0.05) for v in (s_, g_, a_))
+            rd[i0:max(i1, i0 + 1)] += in_tile / max(i1 - i0, 1)
+            wr[i1:max(i2, i1 + 1)] += out_tile / max(i2 - i1, 1)
+        total = rd + wr
+        rate_all.append(total.sum() / span / 1e6)
+        lo, hi = int(0.25 * len(fine)), int(0.75 * len(fine))
+        rate_mid.append(total[lo:hi].sum() / ((hi - lo) * 0.05) / 1e6)
+
+    q = lambda v: "{:.2f} ({:.2f}-{:.2f})".format(*np.percentile(np.concatenate(v), [50, 10, 90]))
+    med = lambda v: float(np.median(v))
+    print(f"timeline: {describe(w)}; {tiles} tiles of {in_tile / 1e3:.2f} kB in, "
+          f"{out_tile / 1e3:.2f} kB out")
+    print(f"per-launch time, {steps} back-to-back launches: libfn.so {ms_prod * 1e3:.2f} us, "
+          f"instrumented build {ms_inst * 1e3:.2f} us")
+    print(f"recorded launches: {launches}, each the last of 10 back-to-back ones")
+    print(f"span, first work-group start to last acknowledged store: median {med(spans):.2f} us "
+          f"(min {min(spans):.2f}, max {max(spans):.2f})")
+    print("tile phases, us, median (10th-90th percentile) over all tiles of all recorded launches:")
+    print(f"  start -> staged (loads landed, decisions drawn): {q(phase['stage'])}")
+    print(f"  staged -> stores issued (first wavefront):       {q(phase['compute'])}")
+    print(f"  issued -> stores acknowledged (all wavefronts):  {q(phase['drain'])}")
+    print(f"  whole life of a work-group:                       {q(phase['life'])}")
+    n = min(len(r) for r in occ_rows)
+    occ = np.median(np.stack([r[:n] for r in occ_rows]), axis=0)
+    print("resident work-groups every 0.5 us (median launch): " +
+          " ".join(str(int(v)) for v in occ))
+    ng = int(np.median([g[0] for g in first_gen]))
+    ret = np.median(np.stack([g[1] for g in first_gen]), axis=0)
+    print(f"first generation: {ng} work-groups start within 0.3 us of the first; they retire at "
+          f"{ret[0]:.2f} / {ret[1]:.2f} / {ret[2]:.2f} us (10th / 50th / 90th percentile)")
+    print(f"last work-group start: {med(last_start):.2f} us; below half the peak occupancy for the "
+          f"last {med(tail_half):.2f} us")
+    print(f"modelled traffic (reads spread over each tile's staging, writes over the rest of its "
+          f"life): {med(rate_all):.2f} TB/s over the span, {med(rate_mid):.2f} TB/s over its "
+          f"middle half")
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The oracle as it stands, on this host's cores, over whole batches of
     the workload (fp32 output) until about budget_s seconds have passed;
@@ -414,6 +520,9 @@ def main() -> int:
     ap.add_argument("--sweep", default=None, metavar="N,N,...",
                     help="time the headline shape at these batch sizes (and the streaming "
                          "reference and a minimal launch) instead of the JSON line")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-tile clock stamps of the headline launch from the instrumented "
+                         "build libfn_timeline.so (a text summary instead of the JSON line)")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--workload", default=None,
                     help="time this workload instead of the headline one (the JSON line then "
@@ -457,6 +566,9 @@ def main() -> int:
     if args.sweep:
         sweep(b, args.steps, args.warmup, args.prewarm_seconds,
               [int(v) for v in args.sweep.split(",")])
+        return 0
+    if args.timeline:
+        timeline(b, args.steps, args.warmup, args.prewarm_seconds)
         return 0
     if shape:
         N, H, W, C = shape

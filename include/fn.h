@@ -238,6 +238,18 @@ int fn_test_cr_ops(int32_t op, const float* a_dev, const float* b_dev, int64_t c
 int fn_test_stream(const void* src_dev, void* dst_dev, int64_t in_bytes, int32_t widen,
                    void* stream);
 
+/* Measurement hook of the instrumented build libfn_timeline.so (the same
+ * sources compiled with FN_TIMELINE=1): every later fused call whose tiles
+ * kernel runs records, for each tile t < tiles, four 64-bit stamps of the
+ * GPU's 100 MHz real-time clock at stamps_dev + 4 t: its work-group's start,
+ * the end of staging (tile loaded and decisions drawn), its stores issued
+ * (first wavefront) and its stores acknowledged (all wavefronts).  The
+ * tile order is the kernel's own (tile t covers the t-th range of rows).
+ * stamps_dev is a caller-owned device buffer of tiles * 32 bytes that must
+ * outlive those calls; tiles = 0 stops recording.  Not thread-safe: one
+ * setting per process.  The product library libfn.so returns FN_EINVAL. */
+int fn_test_timeline(void* stamps_dev, int64_t tiles);
+
 #ifdef __cplusplus
 }
 #endif

@@ -110,6 +110,8 @@ def test_params_and_hooks_validate(b):
     assert L.fn_test_stream(None, None, 24, 2, None) == -1   # a multiple of 16 bytes
     assert L.fn_test_stream(None, None, 0, 4, None) == 0
     assert L.fn_test_stream(None, None, 16, 2, None) == -1   # NULL buffers
+    assert L.fn_test_timeline(None, 0) == -1                 # the product build records nothing
+    assert "timeline" in b.fn_last_error()
     assert L.fn_test_erase_dims(None, None, 0, 8, 8, 0.02, 0.33, 0.3, 3.3, None, None, None,
                                 None) == 0
     assert L.fn_test_erase_dims(None, None, 1, 0, 8, 0.02, 0.33, 0.3, 3.3, None, None, None,
