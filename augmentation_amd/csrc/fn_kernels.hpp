@@ -1016,40 +1016,66 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
   const bool all_elements = kPad4 && (mu & 3) != 0;
   OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out);
 
-  for (int32_t q = (int32_t)threadIdx.x; q < nvec; q += kThreads) {
-    const int64_t e0 = (k0 + q) * E - mu;
-    const int32_t l0 = (int32_t)(e0 - f0);
-    float v[E];
-    if (all_elements) {
-      flat_elements<C, OC, E, kComp>(a, T, s_lds, s_params, head, l0, count, v);
-      if (l0 >= 0 && l0 + E <= count) {
-        store_group<OutT, E, kStoreNt>(out + e0, v);
-      } else {
-#pragma unroll
-        for (int k = 0; k < E; ++k)
-          if (l0 + k >= 0 && l0 + k < count)
-            __builtin_nontemporal_store(to_out<OutT>(v[k]), out + e0 + k);
-      }
-      continue;
-    }
-    if (l0 < 0 || l0 + E > count) continue;  // an end of the tile: second pass
-    const int32_t r = (int32_t)fast_div((uint32_t)l0, a.div_row_out);
-    const int32_t x0 = l0 - r * row_out;
-    if (x0 + E > row_out) continue;  // holds the next row's start: second pass
-    uint32_t slot;
-    int32_t h;
-    tile_row_image(a, T, T.n_first, r, &slot, &h);
-    const Setup cs(a, x0);
-    const SampleParams P = s_params[slot];
-    // one read form per image: shifted dwords serve every alignment, so the
-    // lanes of a wavefront that spans two rows of different alignment do
-    // not split
-    if (P.flip)
-      cs.template values<kSrcFlip>(s_lds, staged_row(a, T, head, row, r), P, h, v);
-    else
-      cs.template values<kSrcBytes>(s_lds, staged_row(a, T, head, row, r), P, h, v);
-    store_group<OutT, E, kStoreNt>(out + e0, v);
+  // a tile of one image reads its decisions into scalar registers once
+  // (measured: 2% faster on padded 299-wide rows, level elsewhere)
+  const bool single = a.images_per_tile == 1;
+  SampleParams Pu;
+  {
+    const SampleParams P0 = s_params[0];
+    Pu.flip = __builtin_amdgcn_readfirstlane(P0.flip);
+    Pu.erase = __builtin_amdgcn_readfirstlane(P0.erase);
+    Pu.i = __builtin_amdgcn_readfirstlane(P0.i);
+    Pu.j = __builtin_amdgcn_readfirstlane(P0.j);
+    Pu.eh = __builtin_amdgcn_readfirstlane(P0.eh);
+    Pu.ew = __builtin_amdgcn_readfirstlane(P0.ew);
   }
+  auto first_pass = [&](auto single_c) {
+    constexpr bool kSingle = decltype(single_c)::value;
+    for (int32_t q = (int32_t)threadIdx.x; q < nvec; q += kThreads) {
+      const int64_t e0 = (k0 + q) * E - mu;
+      const int32_t l0 = (int32_t)(e0 - f0);
+      float v[E];
+      if (all_elements) {
+        flat_elements<C, OC, E, kComp>(a, T, s_lds, s_params, head, l0, count, v);
+        if (l0 >= 0 && l0 + E <= count) {
+          store_group<OutT, E, kStoreNt>(out + e0, v);
+        } else {
+#pragma unroll
+          for (int k = 0; k < E; ++k)
+            if (l0 + k >= 0 && l0 + k < count)
+              __builtin_nontemporal_store(to_out<OutT>(v[k]), out + e0 + k);
+        }
+        continue;
+      }
+      if (l0 < 0 || l0 + E > count) continue;  // an end of the tile: second pass
+      const int32_t r = (int32_t)fast_div((uint32_t)l0, a.div_row_out);
+      const int32_t x0 = l0 - r * row_out;
+      if (x0 + E > row_out) continue;  // holds the next row's start: second pass
+      int32_t h;
+      SampleParams P;
+      if constexpr (kSingle) {
+        h = T.h0 + r;
+        P = Pu;
+      } else {
+        uint32_t slot;
+        tile_row_image(a, T, T.n_first, r, &slot, &h);
+        P = s_params[slot];
+      }
+      const Setup cs(a, x0);
+      // one read form per image: shifted dwords serve every alignment, so the
+      // lanes of a wavefront that spans two rows of different alignment do
+      // not split
+      if (P.flip)
+        cs.template values<kSrcFlip>(s_lds, staged_row(a, T, head, row, r), P, h, v);
+      else
+        cs.template values<kSrcBytes>(s_lds, staged_row(a, T, head, row, r), P, h, v);
+      store_group<OutT, E, kStoreNt>(out + e0, v);
+    }
+  };
+  if (single)
+    first_pass(std::true_type());
+  else
+    first_pass(std::false_type());
   if (all_elements) return;
 
   // second pass: the vector holding the start of row b (b = T.rows: the
