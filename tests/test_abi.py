@@ -38,6 +38,22 @@ def test_library_exports_every_declared_symbol(b):
         assert hasattr(b._lib, name)
 
 
+def test_timeline_build_exports_the_same_symbols_and_validates(b):
+    """The instrumented build libfn_timeline.so (bench.py --timeline) has the
+    product's entry points; its fn_test_timeline checks its arguments."""
+    import os
+    if not os.path.exists(b.TIMELINE_LIB_PATH):
+        pytest.skip("libfn_timeline.so is not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", b.TIMELINE_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(declared_functions())
+    L = b.timeline_library()
+    assert L.fn_test_timeline(None, -1) == -1
+    assert L.fn_test_timeline(None, 5) == -1    # NULL buffer for 5 tiles
+    assert L.fn_test_timeline(None, 0) == 0     # recording off
+
+
 def test_params_struct_is_32_bytes(b):
     import oracle
     assert b.PARAMS_DTYPE.itemsize == 32
