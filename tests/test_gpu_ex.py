@@ -176,6 +176,28 @@ def test_long_launch_equals_its_short_slices(b, C, out_dtype):
     assert torch.equal(whole.view(torch.int16), parts.view(torch.int16))
 
 
+def test_long_strided_launch_equals_its_short_slices(b):
+    """The same for a strided source: centre 224x224 windows of 256x256x3
+    images, 1,030 of them (465 MB moved), against slices of 128 images."""
+    N, S, H, W, C = 1030, 256, 224, 224, 3
+    say(f"long strided launch: N={N}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    src = torch.randint(0, 256, (N, S, S, C), dtype=torch.uint8, device="cuda", generator=g)
+    row, img = S * C, S * S * C
+    first = (16 * S + 16) * C
+    args = (synth.IMAGENET_MEAN, synth.IMAGENET_STD, 0.5, 0.5, 0.02, 0.33, 0.3, 3.3, 21)
+    whole = torch.empty((N, H, W, C), dtype=torch.float16, device="cuda")
+    parts = torch.empty_like(whole)
+    base = src.data_ptr() + first
+    b.fn_fused_normalize_ex(base, row, img, N, H, W, C, *args, 0, 1, whole)
+    for a_ in range(0, N, 128):
+        b_ = min(N, a_ + 128)
+        b.fn_fused_normalize_ex(base + a_ * img, row, img, b_ - a_, H, W, C, *args, a_, 1,
+                                parts[a_:b_])
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), parts.view(torch.int16))
+
+
 @pytest.mark.parametrize("first", [0, 1, 255, 2**32 - 3, 2**40 + 17])
 def test_params_ex_bit_exact(b, first):
     N, H, W = 300, 224, 224
