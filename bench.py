@@ -115,7 +115,7 @@ def host_threads() -> int:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))  # the machine's CPU share for one GPU
+    return max(1, min(n, 16))  # a host's CPU share for one of its eight GPUs
 
 
 def time_launches(launch, steps: int, warmup: int, sets: int, stream, prewarm_s: float,
