@@ -375,13 +375,47 @@ def timeline(b, steps: int, warmup: int, prewarm_s: float, launches: int = 20) -
     tiles = len(runs[0])
     in_tile = w.N * w.H * w.W * w.C / tiles  # bytes per tile, on average
     out_tile = in_tile * 2
-    tick = 0.01  # microseconds per tick of the 100 MHz clock
+    r = timeline_summary(runs, in_tile, out_tile)
+    print(f"timeline: {describe(w)}; {tiles} tiles of {in_tile / 1e3:.2f} kB in, "
+          f"{out_tile / 1e3:.2f} kB out")
+    print(f"per-launch time, {steps} back-to-back launches: libfn.so {ms_prod * 1e3:.2f} us, "
+          f"instrumented build {ms_inst * 1e3:.2f} us")
+    print(f"recorded launches: {launches}, each the last of 10 back-to-back ones")
+    sp = r["span"]
+    print(f"span, first work-group start to last acknowledged store: median {sp[0]:.2f} us "
+          f"(min {sp[1]:.2f}, max {sp[2]:.2f})")
+    print("tile phases, us, median (10th-90th percentile) over all tiles of all recorded launches:")
+    fmt = lambda v: "{:.2f} ({:.2f}-{:.2f})".format(*v)
+    print(f"  start -> staged (loads landed, decisions drawn): {fmt(r['stage'])}")
+    print(f"  staged -> stores issued (first wavefront):       {fmt(r['compute'])}")
+    print(f"  issued -> stores acknowledged (all wavefronts):  {fmt(r['drain'])}")
+    print(f"  whole life of a work-group:                       {fmt(r['life'])}")
+    print("resident work-groups every 0.5 us (median launch): " +
+          " ".join(str(int(v)) for v in r["occupancy"]))
+    ret = r["first_generation_retire"]
+    print(f"first generation: {r['first_generation']} work-groups start within 0.3 us of the first; "
+          f"they retire at {ret[0]:.2f} / {ret[1]:.2f} / {ret[2]:.2f} us (10th / 50th / 90th "
+          f"percentile)")
+    print(f"last work-group start: {r['last_start']:.2f} us; below half the peak occupancy for the "
+          f"last {r['tail_below_half']:.2f} us")
+    print(f"modelled traffic (reads spread over each tile's staging, writes over the rest of its "
+          f"life): {r['tbs_span']:.2f} TB/s over the span, {r['tbs_middle']:.2f} TB/s over its "
+          f"middle half")
 
+
+def timeline_summary(runs, in_tile: float, out_tile: float, tick_us: float = 0.01) -> dict:
+    """Summary of recorded launches: runs holds one array per launch, a row
+    of four clock stamps (start, staged, issued, acknowledged; tick_us per
+    tick) per tile.  Medians over launches; phase figures are (50th, 10th,
+    90th) percentiles over all tiles; times in microseconds from the first
+    start of each launch; modelled traffic in TB/s."""
+    import numpy as np
     spans, phase, occ_rows, first_gen, last_start, tail_half, rate_all, rate_mid = \
         [], {"stage": [], "compute": [], "drain": [], "life": []}, [], [], [], [], [], []
     for d in runs:
+        d = np.asarray(d, dtype=np.float64)
         t0 = d[:, 0].min()
-        S, G, I, A = [(d[:, k] - t0) * tick for k in range(4)]
+        S, G, I, A = [(d[:, k] - t0) * tick_us for k in range(4)]
         span = A.max()
         spans.append(span)
         for name, v in (("stage", G - S), ("compute", I - G), ("drain", A - I), ("life", A - S)):
@@ -396,45 +430,31 @@ def timeline(b, steps: int, warmup: int, prewarm_s: float, launches: int = 20) -
         tail_half.append(span - grid[np.nonzero(active >= peak / 2)[0].max()])
         # modelled traffic: each tile's reads spread evenly over its staging,
         # its writes over the rest of its life
-        fine = np.arange(0.0, span, 0.05)
+        step = 0.05
+        fine = np.arange(0.0, span, step)
         rd = np.zeros_like(fine)
         wr = np.zeros_like(fine)
         for s_, g_, a_ in zip(S, G, A):
-            i0, i1, i2 = (int(v / 0.05) for v in (s_, g_, a_))
+            i0, i1, i2 = (int(v / step) for v in (s_, g_, a_))
             rd[i0:max(i1, i0 + 1)] += in_tile / max(i1 - i0, 1)
             wr[i1:max(i2, i1 + 1)] += out_tile / max(i2 - i1, 1)
         total = rd + wr
         rate_all.append(total.sum() / span / 1e6)
         lo, hi = int(0.25 * len(fine)), int(0.75 * len(fine))
-        rate_mid.append(total[lo:hi].sum() / ((hi - lo) * 0.05) / 1e6)
-
-    q = lambda v: "{:.2f} ({:.2f}-{:.2f})".format(*np.percentile(np.concatenate(v), [50, 10, 90]))
-    med = lambda v: float(np.median(v))
-    print(f"timeline: {describe(w)}; {tiles} tiles of {in_tile / 1e3:.2f} kB in, "
-          f"{out_tile / 1e3:.2f} kB out")
-    print(f"per-launch time, {steps} back-to-back launches: libfn.so {ms_prod * 1e3:.2f} us, "
-          f"instrumented build {ms_inst * 1e3:.2f} us")
-    print(f"recorded launches: {launches}, each the last of 10 back-to-back ones")
-    print(f"span, first work-group start to last acknowledged store: median {med(spans):.2f} us "
-          f"(min {min(spans):.2f}, max {max(spans):.2f})")
-    print("tile phases, us, median (10th-90th percentile) over all tiles of all recorded launches:")
-    print(f"  start -> staged (loads landed, decisions drawn): {q(phase['stage'])}")
-    print(f"  staged -> stores issued (first wavefront):       {q(phase['compute'])}")
-    print(f"  issued -> stores acknowledged (all wavefronts):  {q(phase['drain'])}")
-    print(f"  whole life of a work-group:                       {q(phase['life'])}")
+        rate_mid.append(total[lo:hi].sum() / ((hi - lo) * step) / 1e6)
+    pct = lambda v: tuple(float(x) for x in np.percentile(np.concatenate(v), [50, 10, 90]))
     n = min(len(r) for r in occ_rows)
-    occ = np.median(np.stack([r[:n] for r in occ_rows]), axis=0)
-    print("resident work-groups every 0.5 us (median launch): " +
-          " ".join(str(int(v)) for v in occ))
-    ng = int(np.median([g[0] for g in first_gen]))
-    ret = np.median(np.stack([g[1] for g in first_gen]), axis=0)
-    print(f"first generation: {ng} work-groups start within 0.3 us of the first; they retire at "
-          f"{ret[0]:.2f} / {ret[1]:.2f} / {ret[2]:.2f} us (10th / 50th / 90th percentile)")
-    print(f"last work-group start: {med(last_start):.2f} us; below half the peak occupancy for the "
-          f"last {med(tail_half):.2f} us")
-    print(f"modelled traffic (reads spread over each tile's staging, writes over the rest of its "
-          f"life): {med(rate_all):.2f} TB/s over the span, {med(rate_mid):.2f} TB/s over its "
-          f"middle half")
+    return {
+        "span": (float(np.median(spans)), float(min(spans)), float(max(spans))),
+        "stage": pct(phase["stage"]), "compute": pct(phase["compute"]),
+        "drain": pct(phase["drain"]), "life": pct(phase["life"]),
+        "occupancy": np.median(np.stack([r[:n] for r in occ_rows]), axis=0),
+        "first_generation": int(np.median([g[0] for g in first_gen])),
+        "first_generation_retire": np.median(np.stack([g[1] for g in first_gen]), axis=0),
+        "last_start": float(np.median(last_start)),
+        "tail_below_half": float(np.median(tail_half)),
+        "tbs_span": float(np.median(rate_all)), "tbs_middle": float(np.median(rate_mid)),
+    }
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
