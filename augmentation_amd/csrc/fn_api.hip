@@ -632,7 +632,21 @@ int fused_normalize_impl(const uint8_t* in_u8_dev, const int64_t* strides, int64
       launch_tiles(a, C, out_dtype, comp, nt, (unsigned)a.total_tiles, lds, st);
       return launch_status("fused_tiles_kernel launch");
     }
-    launch_flat(a, C, out_dtype, comp, (unsigned)a.total_tiles, lds, st);
+    {
+      // padded layout: the row-start vectors' values beside the tile, when
+      // they fit in what one work-group may use (the flat kernel reads
+      // edge_offset only for that layout)
+      const int64_t tile_rows = a.images_per_tile == 1 ? a.rows_per_tile
+                                                       : (int64_t)a.images_per_tile * H;
+      const int64_t off = ((int64_t)a.lds_buffer_bytes + 15) / 16 * 16;
+      const int64_t edge_bytes = (tile_rows + 1) * (16 / out_bytes) * (int64_t)sizeof(float);
+      size_t flat_lds = lds;
+      if (out_dtype == FN_OUT_FP16_PAD4 && off + edge_bytes <= lds_all) {
+        a.edge_offset = (int32_t)off;
+        flat_lds = tiles_lds_bytes(dev, (int32_t)(off + edge_bytes));
+      }
+      launch_flat(a, C, out_dtype, comp, (unsigned)a.total_tiles, flat_lds, st);
+    }
     return launch_status("fused_flat_kernel launch");
   }
   if (px > 0) {

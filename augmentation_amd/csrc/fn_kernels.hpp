@@ -147,6 +147,9 @@ struct FusedArgs {
   // (work-group size / chunks per row, when at least 1)
   FastDiv div_cpr;
   int32_t rows_per_pass;
+  // flat kernel: LDS byte offset of the row-start vectors' values (E floats
+  // per row start of the tile); 0: the second pass stores them itself
+  int32_t edge_offset;
   // 1 / (255 std_c) = mul + mul_lo and -mean_c / std_c = nsub + nsub_lo,
   // each the double value split into an fp32 pair (see normalize())
   float mul[4], mul_lo[4];
@@ -1015,6 +1018,13 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
   // padded outputs off a pixel boundary: no vector starts at a pixel
   const bool all_elements = kPad4 && (mu & 3) != 0;
   OutT* __restrict__ out = reinterpret_cast<OutT*>(a.out);
+  // the padded layout hands its row-start vectors to the first pass
+  // through LDS (second_pass below); the other layouts measured faster
+  // storing them in the second pass
+  float* edge = nullptr;
+  if constexpr (kPad4) {
+    if (a.edge_offset > 0 && !all_elements) edge = reinterpret_cast<float*>(s_lds + a.edge_offset);
+  }
 
   // a tile of one image reads its decisions into scalar registers once
   // (measured: 2% faster on padded 299-wide rows, level elsewhere)
@@ -1050,7 +1060,15 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
       if (l0 < 0 || l0 + E > count) continue;  // an end of the tile: second pass
       const int32_t r = (int32_t)fast_div((uint32_t)l0, a.div_row_out);
       const int32_t x0 = l0 - r * row_out;
-      if (x0 + E > row_out) continue;  // holds the next row's start: second pass
+      if (x0 + E > row_out) {
+        // holds the next row's start: the second pass has left its values
+        // in LDS (or stores it itself when they do not fit there)
+        if (edge == nullptr) continue;
+#pragma unroll
+        for (int k = 0; k < E; ++k) v[k] = edge[(r + 1) * E + k];
+        store_group<OutT, E, kStoreNt>(out + e0, v);
+        continue;
+      }
       int32_t h;
       SampleParams P;
       if constexpr (kSingle) {
@@ -1072,33 +1090,52 @@ __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(Fused
       store_group<OutT, E, kStoreNt>(out + e0, v);
     }
   };
+  // second pass: the vector holding the start of row b (b = T.rows: the
+  // tile's end) when that is not its first element, one element per lane
+  // (E lanes per vector); a vector holding several row starts is done at
+  // the first of them.  A vector inside the tile goes to LDS (edge) when
+  // there is room, for the first pass to store it with its neighbours: a
+  // line written by one store instruction leaves L2 whole, one written in
+  // two parts a microsecond apart often leaves in two.
+  auto second_pass = [&]() {
+    const int32_t n2 = (T.rows + 1) * E;
+    for (int32_t t = (int32_t)threadIdx.x; t < n2; t += kThreads) {
+      const int32_t b = t / E;
+      const int32_t k = t - b * E;
+      const int64_t e = f0 + (int64_t)b * row_out + mu;  // shifted element index
+      if (e % E == 0) continue;
+      const int64_t kv = e / E;
+      if (b > 0) {
+        const int64_t ep = e - row_out;
+        if (ep % E != 0 && ep / E == kv) continue;
+      }
+      const int64_t e0 = kv * E - mu;
+      const int32_t lv = (int32_t)(e0 - f0);
+      const int32_t l = lv + k;
+      if (l < 0 || l >= count) continue;
+      const float y = flat_element<C, OC, kComp>(a, T, s_lds, s_params, head, l);
+      if (edge != nullptr && lv >= 0 && lv + E <= count)
+        edge[b * E + k] = y;
+      else
+        __builtin_nontemporal_store(to_out<OutT>(y), out + e0 + k);
+    }
+  };
+  if (all_elements) {
+    if (single)
+      first_pass(std::true_type());
+    else
+      first_pass(std::false_type());
+    return;
+  }
+  if (edge != nullptr) {
+    second_pass();
+    __syncthreads();
+  }
   if (single)
     first_pass(std::true_type());
   else
     first_pass(std::false_type());
-  if (all_elements) return;
-
-  // second pass: the vector holding the start of row b (b = T.rows: the
-  // tile's end) when that is not its first element, one element per lane
-  // (E lanes per vector); a vector holding several row starts is done at
-  // the first of them
-  const int32_t n2 = (T.rows + 1) * E;
-  for (int32_t t = (int32_t)threadIdx.x; t < n2; t += kThreads) {
-    const int32_t b = t / E;
-    const int32_t k = t - b * E;
-    const int64_t e = f0 + (int64_t)b * row_out + mu;  // shifted element index
-    if (e % E == 0) continue;
-    const int64_t kv = e / E;
-    if (b > 0) {
-      const int64_t ep = e - row_out;
-      if (ep % E != 0 && ep / E == kv) continue;
-    }
-    const int64_t e0 = kv * E - mu;
-    const int32_t l = (int32_t)(e0 - f0) + k;
-    if (l < 0 || l >= count) continue;
-    __builtin_nontemporal_store(
-        to_out<OutT>(flat_element<C, OC, kComp>(a, T, s_lds, s_params, head, l)), out + e0 + k);
-  }
+  if (edge == nullptr) second_pass();
 }
 
 // ---------------------------------------------------------------------------
