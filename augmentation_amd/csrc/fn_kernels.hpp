@@ -991,7 +991,10 @@ __device__ __forceinline__ void flat_elements(const FusedArgs& a, const Tile& T,
 // elements are stored: the tile next to it stores the rest of a vector they
 // share, so no byte is written twice.  All stores are non-temporal
 // (kStoreNt): the lines that the two passes (or two tiles) write in parts
-// then merge in L2 instead of reaching memory as partial writes.
+// then merge in L2 instead of reaching memory as partial writes.  For the
+// padded layout the second pass runs first and leaves the values of the
+// row-start vectors inside the tile in LDS (a.edge_offset), and the first
+// pass stores them with their neighbours.
 template <int C, typename OutT, bool kPad4, bool kComp>
 __global__ void __launch_bounds__(tiles_threads<OutT>()) fused_flat_kernel(FusedArgs a) {
   constexpr int kThreads = tiles_threads<OutT>();
