@@ -110,13 +110,25 @@ def _check(rc: int) -> int:
     return rc
 
 
+_FLOATS: dict = {}  # recent constant arrays: the library only reads them during the call
+
+
 def _host_floats(v, C: int):
+    try:
+        key = (C, v if isinstance(v, tuple) else tuple(v) if hasattr(v, "__len__") else v)
+        a = _FLOATS.get(key)
+        if a is not None:
+            return a
+    except TypeError:  # unhashable values
+        key = None
     a = (ctypes.c_float * C)()
     vals = list(v) if hasattr(v, "__len__") else [v] * C
     if len(vals) != C:
         raise ValueError(f"expected {C} values, got {len(vals)}")
     for k, x in enumerate(vals):
         a[k] = float(x)
+    if key is not None and len(_FLOATS) < 64:
+        _FLOATS[key] = a
     return a
 
 
