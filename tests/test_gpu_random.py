@@ -18,7 +18,7 @@ from test_gpu_parity import say
 
 pytestmark = pytest.mark.gpu
 
-CASES = 200
+CASES = 1000
 
 
 @pytest.fixture(scope="module")
@@ -85,7 +85,7 @@ def test_random_case(b, k):
     check(as_values(raw, (N, H, W, C), c["out_dtype"]), ref, C, c["out_dtype"], f"case {k}", False)
 
 
-WIDE_CASES = 30
+WIDE_CASES = 100
 
 
 @pytest.mark.parametrize("k", range(WIDE_CASES))
