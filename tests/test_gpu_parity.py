@@ -492,3 +492,55 @@ def test_concurrent_calls_on_two_streams(b):
         torch.cuda.synchronize()
         assert torch.equal(o16.view(torch.int16), ref16.view(torch.int16))
         assert torch.equal(o32.view(torch.int32), ref32.view(torch.int32))
+
+
+def test_calls_from_several_host_threads(b):
+    """The host side is reentrant: four threads, each on its own stream with
+    its own constants, output type and seed (so each thread's memo of the
+    one-fma check and its error buffer differ), call the library 25 times
+    each while the others do; every output equals its serial result, and an
+    invalid call in one thread reports its own error there."""
+    import threading
+    w = synth.WORKLOADS["imagenet_train"]
+    xt = torch.from_numpy(w.make_input()[:32]).cuda()
+    N = xt.shape[0]
+    jobs = [((0.485, 0.456, 0.406), (0.229, 0.224, 0.225), 1, 11),
+            ((0.4, 0.4, 0.4), (0.2, 0.2, 0.2), 0, 12),
+            ((0.5, 0.5, 0.5), (0.25, 0.25, 0.25), 2, 13),
+            ((0.3, 0.6, 0.1), (0.3, 0.17, 0.45), 1, 14)]
+    refs = []
+    for mean, std, od, seed in jobs:
+        refs.append(b.fused_normalize(xt, mean, std, 0.5, 0.5, (0.02, 0.33), (0.3, 3.3), seed, od))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(j):
+        mean, std, od, seed = jobs[j]
+        s = torch.cuda.Stream()
+        out = torch.empty_like(refs[j])
+        try:
+            for it in range(25):
+                b.fused_normalize(xt, mean, std, 0.5, 0.5, (0.02, 0.33), (0.3, 3.3), seed, od,
+                                  out=out, stream=s)
+                if it % 5 == 0:
+                    try:  # flip_p = 2: rejected by the library before any launch
+                        b.fn_fused_normalize(xt, N, w.H, w.W, w.C, mean, std, 2.0, 0.5, 0.02,
+                                             0.33, 0.3, 3.3, seed, od, out, s)
+                        errors.append((j, "invalid call accepted"))
+                    except b.FnError as e:
+                        if "flip_p must be in [0, 1]" not in str(e):
+                            errors.append((j, str(e)))
+                s.synchronize()
+                view = torch.int32 if od == 0 else torch.int16
+                if not torch.equal(out.view(view), refs[j].view(view)):
+                    errors.append((j, f"iteration {it} differs"))
+        except Exception as e:  # noqa: BLE001
+            errors.append((j, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors[:5]
